@@ -1,0 +1,221 @@
+"""Seeded synthetic inputs for the KDA layer core.
+
+This module only draws random numbers with the shapes and distributions of
+the workloads below; it holds none of the layer's arithmetic and is the one
+piece shared by the GPU path's tests/benchmark and the CPU oracle.
+
+Every tensor is drawn block by block from numpy's PCG64, seeded with
+SeedSequence([workload_seed, tensor_id, seq, head]), so any (sequence, head)
+slice can be regenerated on its own.  Values are drawn in float32 (float64
+for the gates, then rounded to float32); tensors stored as bf16 are rounded
+to nearest-even bf16 here and returned as float32 arrays holding exactly
+bf16-representable values, so both sides see identical inputs.
+
+Workloads (H heads of width d = 128):
+  core_fp32   B=1, H=2, T=256; fp32; q, k ~ N(0,1) then unit-normalised per
+              (token, head); v ~ N(0,1); log alpha = -5*sigmoid(x), x ~ N(0,1);
+              beta = sigmoid(y), y ~ N(0,1); S0 = 0; no prologue/epilogue.
+  prefill_4x4096   B=4, H=96, T=4096; bf16 q, k, v, g ~ N(0,1); conv weights
+              ~ N(0, 0.5^2) fp32; gates as above; S0 = 0; prologue + epilogue.
+  prefill_131072   one sequence of T=131072, as above, S0 ~ N(0, 0.02^2).
+  decode_256  B=256 requests, one token each; state ~ N(0, 0.02^2) fp32;
+              bf16 q, k, v, g ~ N(0,1); conv caches ~ N(0,1) bf16.
+  varlen_64   64 sequences, lengths lognormal with mean 8192 and sigma 1
+              (mu = ln 8192 - 1/2), rounded and clipped to [16, 65536];
+              per-sequence S0 ~ N(0, 0.02^2).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+D = 128
+
+# tensor ids inside one workload's seed space
+T_Q, T_K, T_V, T_G, T_ALPHA, T_BETA, T_CONVW, T_CONVIN, T_STATE, T_LENS = range(10)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    u = a.view(np.uint32)
+    r = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _rng(seed: int, tensor: int, n: int = 0, h: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tensor, n, h])))
+
+
+@dataclass
+class PrefillSpec:
+    lens: Sequence[int]
+    heads: int = 96
+    io: str = "bf16"               # "bf16" or "f32"
+    prologue: bool = True
+    epilogue: bool = True
+    state_std: Optional[float] = None   # None -> S0 = 0 (no state given)
+    conv_in: bool = False          # draw a conv history per sequence
+    decay: str = "fast"            # "fast": -5*sigmoid(x); "slow": -5*sigmoid(x-6); "none": 0
+    unit_qk: bool = False          # normalise q, k per (token, head) (prologue off)
+    seed: int = 1
+    name: str = "custom"
+
+    @property
+    def total(self) -> int:
+        return int(np.sum(self.lens))
+
+
+def _fill_blocks(out: np.ndarray, seed: int, tensor: int, cu: np.ndarray, draw) -> None:
+    N = len(cu) - 1
+    H = out.shape[1]
+    for n in range(N):
+        s, e = int(cu[n]), int(cu[n + 1])
+        if e == s:
+            continue
+        for h in range(H):
+            out[s:e, h] = draw(_rng(seed, tensor, n, h), (e - s,) + out.shape[2:])
+
+
+def _normal32(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def _log_alpha(mode: str):
+    def draw(rng, shape):
+        x = rng.standard_normal(shape)
+        if mode == "fast":
+            return (-5.0 / (1.0 + np.exp(-x))).astype(np.float32)
+        if mode == "slow":
+            return (-5.0 / (1.0 + np.exp(-(x - 6.0)))).astype(np.float32)
+        if mode == "none":
+            return np.zeros(shape, np.float32)
+        raise ValueError(mode)
+    return draw
+
+
+def _beta(rng, shape):
+    y = rng.standard_normal(shape)
+    return (1.0 / (1.0 + np.exp(-y))).astype(np.float32)
+
+
+def _unit(rng, shape):
+    x = rng.standard_normal(shape)
+    return (x / np.linalg.norm(x, axis=-1, keepdims=True)).astype(np.float32)
+
+
+def gen_prefill(spec: PrefillSpec) -> Dict[str, np.ndarray]:
+    """Draw every input of one prefill call as host float32 arrays.
+
+    Keys: cu_seqlens (int32 [N+1]), q, k, v, g ([T,H,128]), log_alpha ([T,H,128]),
+    beta ([T,H]), conv_w ([3,H*128,4]), conv_in ([N,3,3,H*128]) and state_in
+    ([N,H,128,128]) -- the last four only when the spec asks for them.
+    """
+    lens = np.asarray(spec.lens, dtype=np.int64)
+    cu = np.zeros(len(lens) + 1, np.int64)
+    cu[1:] = np.cumsum(lens)
+    T, H, N = int(cu[-1]), spec.heads, len(lens)
+    sd = spec.seed
+    out: Dict[str, np.ndarray] = {"cu_seqlens": cu.astype(np.int32)}
+    for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V)):
+        a = np.empty((T, H, D), np.float32)
+        draw = _unit if (spec.unit_qk and name != "v") else _normal32
+        _fill_blocks(a, sd, tid, cu, draw)
+        out[name] = a
+    if spec.epilogue:
+        a = np.empty((T, H, D), np.float32)
+        _fill_blocks(a, sd, T_G, cu, _normal32)
+        out["g"] = a
+    a = np.empty((T, H, D), np.float32)
+    _fill_blocks(a, sd, T_ALPHA, cu, _log_alpha(spec.decay))
+    out["log_alpha"] = a
+    b = np.empty((T, H), np.float32)
+    _fill_blocks(b, sd, T_BETA, cu, _beta)
+    out["beta"] = b
+    if spec.prologue:
+        out["conv_w"] = (_rng(sd, T_CONVW).standard_normal((3, H * D, 4)) * 0.5).astype(np.float32)
+        if spec.conv_in:
+            ci = np.empty((N, 3, 3, H * D), np.float32)
+            for n in range(N):
+                ci[n] = _rng(sd, T_CONVIN, n).standard_normal((3, 3, H * D), dtype=np.float32)
+            out["conv_in"] = ci
+    if spec.state_std is not None:
+        st = np.empty((N, H, D, D), np.float32)
+        for n in range(N):
+            for h in range(H):
+                st[n, h] = _rng(sd, T_STATE, n, h).standard_normal((D, D)) * spec.state_std
+        out["state_in"] = st
+    if spec.io == "bf16":
+        for key in ("q", "k", "v", "g", "conv_in"):
+            if key in out:
+                out[key] = bf16_round(out[key])
+    return out
+
+
+@dataclass
+class DecodeSpec:
+    batch: int = 256
+    heads: int = 96
+    io: str = "bf16"
+    state_std: float = 0.02
+    decay: str = "fast"
+    seed: int = 3
+    name: str = "decode_256"
+
+
+def gen_decode(spec: DecodeSpec) -> Dict[str, np.ndarray]:
+    """Inputs of one decode step: q, k, v, g, log_alpha [B,H,128]; beta [B,H];
+    state [B,H,128,128]; conv_state [B,3,3,H*128]; conv_w [3,H*128,4]."""
+    B, H, sd = spec.batch, spec.heads, spec.seed
+    cu = np.arange(B + 1, dtype=np.int64)
+    out: Dict[str, np.ndarray] = {}
+    for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V), ("g", T_G)):
+        a = np.empty((B, H, D), np.float32)
+        _fill_blocks(a, sd, tid, cu, _normal32)
+        out[name] = a
+    a = np.empty((B, H, D), np.float32)
+    _fill_blocks(a, sd, T_ALPHA, cu, _log_alpha(spec.decay))
+    out["log_alpha"] = a
+    b = np.empty((B, H), np.float32)
+    _fill_blocks(b, sd, T_BETA, cu, _beta)
+    out["beta"] = b
+    out["conv_w"] = (_rng(sd, T_CONVW).standard_normal((3, H * D, 4)) * 0.5).astype(np.float32)
+    cs = np.empty((B, 3, 3, H * D), np.float32)
+    for n in range(B):
+        cs[n] = _rng(sd, T_CONVIN, n).standard_normal((3, 3, H * D), dtype=np.float32)
+    out["conv_state"] = cs
+    st = np.empty((B, H, D, D), np.float32)
+    for n in range(B):
+        rng = _rng(sd, T_STATE, n)
+        st[n] = rng.standard_normal((H, D, D), dtype=np.float32) * np.float32(spec.state_std)
+    out["state"] = st
+    if spec.io == "bf16":
+        for key in ("q", "k", "v", "g", "conv_state"):
+            out[key] = bf16_round(out[key])
+    return out
+
+
+def varlen_lengths(n_seqs: int = 64, mean: float = 8192.0, sigma: float = 1.0,
+                   lo: int = 16, hi: int = 65536, seed: int = 4) -> List[int]:
+    """Lognormal lengths whose distribution mean is `mean` (mu = ln mean - sigma^2/2)."""
+    z = _rng(seed, T_LENS).standard_normal(n_seqs)
+    mu = np.log(mean) - 0.5 * sigma * sigma
+    return [int(x) for x in np.clip(np.rint(np.exp(mu + sigma * z)), lo, hi)]
+
+
+def workload(name: str) -> object:
+    """The named workloads; see the module docstring."""
+    if name == "core_fp32":
+        return PrefillSpec(lens=[256], heads=2, io="f32", prologue=False, epilogue=False,
+                           unit_qk=True, seed=0, name=name)
+    if name == "prefill_4x4096":
+        return PrefillSpec(lens=[4096] * 4, heads=96, seed=1, name=name)
+    if name == "prefill_131072":
+        return PrefillSpec(lens=[131072], heads=96, state_std=0.02, seed=2, name=name)
+    if name == "decode_256":
+        return DecodeSpec(batch=256, heads=96, seed=3, name=name)
+    if name == "varlen_64":
+        return PrefillSpec(lens=varlen_lengths(), heads=96, state_std=0.02, seed=4, name=name)
+    raise KeyError(name)

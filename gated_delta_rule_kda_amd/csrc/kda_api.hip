@@ -1,0 +1,207 @@
+// kda_api.hip -- the C ABI of libkda.so: host-side validation, workspace
+// sizing and dispatch to the gfx950 kernels.  Nothing here synchronises with
+// the device; a call only enqueues work on the caller's stream.
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+// Sequences are ranked longest first so that, in a packed batch of very
+// different lengths, the workgroups with the longest sequential scans start
+// first.  The rank of sequence i is the number of sequences that are longer,
+// or equally long with a smaller index; order[rank] = i.  One launch of
+// ceil(N/256) workgroups, each staging all N lengths in LDS.
+constexpr int ORDER_MAX_SEQS = 8192;  // beyond this the natural order is used
+
+__global__ __launch_bounds__(256) void order_kernel(const int32_t *cu, int32_t n, int32_t *order) {
+    __shared__ int32_t len[ORDER_MAX_SEQS];
+    for (int i = threadIdx.x; i < n; i += blockDim.x) len[i] = cu[i + 1] - cu[i];
+    __syncthreads();
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int32_t li = len[i];
+    int32_t rank = 0;
+    for (int j = 0; j < n; ++j) {
+        const int32_t lj = len[j];
+        rank += (lj > li) || (lj == li && j < i);
+    }
+    order[rank] = i;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool trace_enabled() {
+    static const bool on = [] {
+        const char *e = getenv("KDA_TRACE");
+        return e && e[0] && e[0] != '0';
+    }();
+    return on;
+}
+
+kda_status check_config(const kda_config *cfg) {
+    if (!cfg) return KDA_ERR_INVALID_ARGUMENT;
+    if (cfg->head_dim != D) return KDA_ERR_UNSUPPORTED;
+    if (cfg->num_heads <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (cfg->io_dtype != KDA_DTYPE_F32 && cfg->io_dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+    if (cfg->out_dtype != KDA_DTYPE_F32 && cfg->out_dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
+    if ((cfg->prologue != 0 && cfg->prologue != 1) || (cfg->epilogue != 0 && cfg->epilogue != 1))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (cfg->algo != KDA_ALGO_AUTO && cfg->algo != KDA_ALGO_RECURRENT && cfg->algo != KDA_ALGO_CHUNKED)
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (!isfinite(cfg->scale) || !(cfg->l2_eps >= 0.f) || !(cfg->rms_eps >= 0.f) ||
+        !isfinite(cfg->l2_eps) || !isfinite(cfg->rms_eps))
+        return KDA_ERR_INVALID_ARGUMENT;
+    return KDA_OK;
+}
+
+// A required pointer must be non-null; every given pointer must be 16-byte aligned.
+bool ok_ptr(const void *p, bool required) {
+    if (!p) return !required;
+    return aligned16(p);
+}
+
+kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+size_t order_workspace_bytes(int32_t n) {
+    if (n <= 1 || n > ORDER_MAX_SEQS) return 0;
+    return (static_cast<size_t>(n) * sizeof(int32_t) + 255u) & ~static_cast<size_t>(255u);
+}
+
+hipError_t launch_order(const int32_t *cu_seqlens, int32_t n, int32_t *order, hipStream_t s) {
+    hipLaunchKernelGGL(order_kernel, dim3((n + 255) / 256), dim3(256), 0, s, cu_seqlens, n, order);
+    return hipGetLastError();
+}
+
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" {
+
+void kda_config_init(kda_config *cfg, int32_t num_heads) {
+    if (!cfg) return;
+    cfg->num_heads = num_heads;
+    cfg->head_dim = D;
+    cfg->io_dtype = KDA_DTYPE_BF16;
+    cfg->out_dtype = KDA_DTYPE_BF16;
+    cfg->prologue = 1;
+    cfg->epilogue = 1;
+    cfg->algo = KDA_ALGO_AUTO;
+    cfg->scale = 1.0f / sqrtf(static_cast<float>(D));
+    cfg->l2_eps = 1e-6f;
+    cfg->rms_eps = 1e-6f;
+}
+
+kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens,
+                                      size_t *bytes) {
+    kda_status st = check_config(cfg);
+    if (st != KDA_OK) return st;
+    if (!bytes || num_seqs <= 0 || total_tokens < 0) return KDA_ERR_INVALID_ARGUMENT;
+    *bytes = order_workspace_bytes(num_seqs);
+    return KDA_OK;
+}
+
+kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *hip_stream) {
+    kda_status st = check_config(cfg);
+    if (st != KDA_OK) return st;
+    if (!a || a->num_seqs <= 0 || a->total_tokens < 0) return KDA_ERR_INVALID_ARGUMENT;
+    const int64_t H = cfg->num_heads;
+    if (static_cast<int64_t>(a->num_seqs) * H > 0x7fffffffLL) return KDA_ERR_UNSUPPORTED;
+    const bool tok = a->total_tokens > 0;
+    if (!ok_ptr(a->cu_seqlens, true) || !ok_ptr(a->q, tok) || !ok_ptr(a->k, tok) ||
+        !ok_ptr(a->v, tok) || !ok_ptr(a->log_alpha, tok) || !ok_ptr(a->beta, tok) ||
+        !ok_ptr(a->o, tok) || !ok_ptr(a->g, tok && cfg->epilogue) ||
+        !ok_ptr(a->conv_w, cfg->prologue != 0) || !ok_ptr(a->conv_in, false) ||
+        !ok_ptr(a->conv_out, false) || !ok_ptr(a->rms_w, false) || !ok_ptr(a->state_in, false) ||
+        !ok_ptr(a->state_out, false) || !ok_ptr(a->workspace, false))
+        return KDA_ERR_INVALID_ARGUMENT;
+    const size_t need = order_workspace_bytes(a->num_seqs);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+    int algo = cfg->algo;
+    if (algo == KDA_ALGO_AUTO) algo = cfg->io_dtype == KDA_DTYPE_BF16 ? KDA_ALGO_CHUNKED : KDA_ALGO_RECURRENT;
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    int32_t *order = need > 0 ? static_cast<int32_t *>(a->workspace) : nullptr;
+    if (order) {
+        st = from_hip(launch_order(a->cu_seqlens, a->num_seqs, order, s));
+        if (st != KDA_OK) return st;
+    }
+    LayerParams p{};
+    p.H = cfg->num_heads;
+    p.num_items = a->num_seqs * cfg->num_heads;
+    p.cu_seqlens = a->cu_seqlens;
+    p.order = order;
+    p.q = a->q; p.k = a->k; p.v = a->v; p.g = cfg->epilogue ? a->g : nullptr;
+    p.log_alpha = a->log_alpha; p.beta = a->beta;
+    p.conv_w = cfg->prologue ? a->conv_w : nullptr;
+    p.rms_w = a->rms_w;
+    p.conv_in = cfg->prologue ? a->conv_in : nullptr;
+    p.conv_out = cfg->prologue ? a->conv_out : nullptr;
+    p.state_in = a->state_in; p.state_out = a->state_out; p.o = a->o;
+    p.scale = cfg->scale; p.l2_eps = cfg->l2_eps; p.rms_eps = cfg->rms_eps;
+    p.prologue = cfg->prologue; p.epilogue = cfg->epilogue;
+    if (trace_enabled())
+        fprintf(stderr, "[kda] prefill N=%d H=%d T=%lld io=%d out=%d algo=%d prologue=%d epilogue=%d\n",
+                a->num_seqs, cfg->num_heads, static_cast<long long>(a->total_tokens), cfg->io_dtype,
+                cfg->out_dtype, algo, cfg->prologue, cfg->epilogue);
+    hipError_t e = algo == KDA_ALGO_CHUNKED ? launch_chunked(p, cfg->io_dtype, cfg->out_dtype, s)
+                                            : launch_recurrent(p, cfg->io_dtype, cfg->out_dtype, s);
+    return from_hip(e);
+}
+
+kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *a, void *hip_stream) {
+    kda_status st = check_config(cfg);
+    if (st != KDA_OK) return st;
+    if (!a || a->batch <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (static_cast<int64_t>(a->batch) * cfg->num_heads > 0x7fffffffLL) return KDA_ERR_UNSUPPORTED;
+    if (!ok_ptr(a->q, true) || !ok_ptr(a->k, true) || !ok_ptr(a->v, true) ||
+        !ok_ptr(a->log_alpha, true) || !ok_ptr(a->beta, true) || !ok_ptr(a->o, true) ||
+        !ok_ptr(a->state, true) || !ok_ptr(a->g, cfg->epilogue != 0) ||
+        !ok_ptr(a->conv_w, cfg->prologue != 0) || !ok_ptr(a->conv_state, cfg->prologue != 0) ||
+        !ok_ptr(a->rms_w, false) || !ok_ptr(a->slots, false))
+        return KDA_ERR_INVALID_ARGUMENT;
+    LayerParams p{};
+    p.H = cfg->num_heads;
+    p.num_items = a->batch * cfg->num_heads;
+    p.cu_seqlens = nullptr;
+    p.slots = a->slots;
+    p.q = a->q; p.k = a->k; p.v = a->v; p.g = cfg->epilogue ? a->g : nullptr;
+    p.log_alpha = a->log_alpha; p.beta = a->beta;
+    p.conv_w = cfg->prologue ? a->conv_w : nullptr;
+    p.rms_w = a->rms_w;
+    p.conv_in = cfg->prologue ? a->conv_state : nullptr;
+    p.conv_out = cfg->prologue ? a->conv_state : nullptr;
+    p.state_in = a->state; p.state_out = a->state; p.o = a->o;
+    p.scale = cfg->scale; p.l2_eps = cfg->l2_eps; p.rms_eps = cfg->rms_eps;
+    p.prologue = cfg->prologue; p.epilogue = cfg->epilogue;
+    if (trace_enabled())
+        fprintf(stderr, "[kda] decode B=%d H=%d io=%d out=%d\n", a->batch, cfg->num_heads,
+                cfg->io_dtype, cfg->out_dtype);
+    return from_hip(launch_recurrent(p, cfg->io_dtype, cfg->out_dtype, static_cast<hipStream_t>(hip_stream)));
+}
+
+const char *kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case KDA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+uint32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+size_t kda_state_bytes(int32_t num_heads) {
+    return num_heads > 0 ? static_cast<size_t>(num_heads) * D * D * sizeof(float) : 0;
+}
+
+}  // extern "C"

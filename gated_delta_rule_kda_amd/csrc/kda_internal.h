@@ -1,0 +1,75 @@
+// kda_internal.h -- declarations shared by the host dispatcher and the
+// kernels of libkda.so (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+constexpr int D = KDA_HEAD_DIM;  // d_k = d_v = 128
+constexpr int CONV_HIST = 3;     // kernel size 4 minus the current token
+
+// Everything a kernel needs to know about one call.  Pointers are device
+// pointers; activations are token-major [tokens][H][128].
+struct LayerParams {
+    int32_t H;
+    int32_t num_items;           // work items = sequences (or requests) x heads
+    const int32_t *cu_seqlens;   // prefill: [N+1]; decode: NULL (one token per request)
+    const int32_t *slots;        // decode: state / conv row of each request (NULL = identity)
+    const int32_t *order;        // prefill: longest-first sequence order (NULL = identity)
+    const void *q, *k, *v, *g;
+    const float *log_alpha, *beta;
+    const float *conv_w, *rms_w;
+    const void *conv_in;
+    void *conv_out;
+    const float *state_in;
+    float *state_out;
+    void *o;
+    float scale, l2_eps, rms_eps;
+    int32_t prologue, epilogue;
+};
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_recurrent(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s);
+hipError_t launch_chunked(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s);
+hipError_t launch_order(const int32_t *cu_seqlens, int32_t n, int32_t *order, hipStream_t s);
+size_t order_workspace_bytes(int32_t n);
+
+// ------------------------------------------------------------ device helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct IoTraits;
+template <> struct IoTraits<float> {
+    static __device__ __forceinline__ float load(const void *p, size_t i) {
+        return static_cast<const float *>(p)[i];
+    }
+    static __device__ __forceinline__ void store(void *p, size_t i, float x) {
+        static_cast<float *>(p)[i] = x;
+    }
+};
+template <> struct IoTraits<uint16_t> {  // bf16 stored as raw bits
+    static __device__ __forceinline__ float load(const void *p, size_t i) {
+        return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
+    }
+    static __device__ __forceinline__ void store(void *p, size_t i, float x) {
+        static_cast<uint16_t *>(p)[i] = f32_to_bf16(x);
+    }
+};
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + __expf(-x)); }
+
+}  // namespace kda

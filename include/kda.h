@@ -1,0 +1,155 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) core.
+ *
+ * What is computed (per head h, per token t of each packed sequence), as the
+ * KDA step list of the OpenModelAtlas page "Kimi K3 - KDA layer" states it:
+ *
+ *   prologue  x^c_t = SiLU(sum_{j=0..3} w_x[j] * x^p_{t-j})  for x in {q, k, v}
+ *             q^ = q^c / ||q^c||,  k^ = k^c / ||k^c||  (per head, 128 channels;
+ *             v gets no normalisation -- "Inside Kimi K3: How KDA, AttnRes,
+ *             and 896 Experts Work", section "Short convolutions give KDA
+ *             local order before recurrence")
+ *   decay     S <- Diag(alpha_t) S,  alpha_t = exp(log_alpha_t) per key channel
+ *   delta     S <- S + beta_t k^ (v - S^T k^)^T
+ *   read      o~ = S^T q^ * scale   (scale = 1/sqrt(128))
+ *   epilogue  o = sigmoid(g) * RMSNorm(o~)  (per head over the 128 value
+ *             channels, gain w_rms shared by all heads, no bias)
+ *
+ * The order decay -> predict -> error -> write -> read is the one given in
+ * section "KDA writes corrections into a recurrent matrix" of the same
+ * "Inside Kimi K3" page; alpha scales row i of S (the key channel) as in
+ * "Kimi K3: Architecture and SGLang Day-0 Support", "Math details: how KDA
+ * gates and rewrites the same S".
+ *
+ * Conventions shared by every entry point:
+ *  - d_k = d_v = 128 (KDA_HEAD_DIM); H = num_heads heads; all activations are
+ *    token-major [tokens][H][128] (the projection output [tokens][H*128]).
+ *  - The recurrent state is fp32 [.., H, 128, 128], S[i][j], i = key channel
+ *    (row), j = value channel, row-major.
+ *  - Conv caches are [N][3 streams q,k,v][3 taps, oldest first][H*128] in
+ *    io_dtype: the last three pre-conv inputs of each stream.  Conv weights
+ *    are fp32 [3 streams][H*128][4]; tap j multiplies x_{t-j}; no bias.
+ *  - log_alpha is fp32 and must lie in [-5, 0] (the log-decay floor of "The
+ *    lower bound on decay is a hardware decision", "Inside Kimi K3"); beta is
+ *    fp32 in [0, 1].  These are documented preconditions, not checked on the
+ *    device: values outside them may produce inf/NaN in the chunked kernel.
+ *  - Pointers are device pointers unless marked "host".  Every device pointer
+ *    must be 16-byte aligned.  The caller owns every buffer; the library
+ *    allocates no device memory in these calls and keeps no pointer after it
+ *    returns.
+ *  - Calls are asynchronous on the given HIP stream (0 = the null stream),
+ *    reentrant and thread-safe; results are valid once the stream reaches
+ *    the call.  Host-side validation failures return an error status and
+ *    enqueue nothing.  No call aborts or throws.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128
+#define KDA_ABI_VERSION 1u
+
+/* Status codes. */
+typedef int32_t kda_status;
+#define KDA_OK 0
+#define KDA_ERR_INVALID_ARGUMENT 1   /* null / misaligned pointer, bad size or enum */
+#define KDA_ERR_UNSUPPORTED 2        /* head_dim != 128 or an unsupported combination */
+#define KDA_ERR_WORKSPACE_TOO_SMALL 3
+#define KDA_ERR_HIP 4                /* a HIP runtime call or launch failed */
+
+/* Element types of activations. */
+#define KDA_DTYPE_F32 0
+#define KDA_DTYPE_BF16 1
+
+/* Prefill algorithm. AUTO picks CHUNKED for bf16 inputs and RECURRENT for fp32. */
+#define KDA_ALGO_AUTO 0
+#define KDA_ALGO_RECURRENT 1   /* token-sequential fp32 recurrence */
+#define KDA_ALGO_CHUNKED 2     /* 64-token chunks on MFMA, split-fp16 operands */
+
+typedef struct {
+    int32_t num_heads;   /* H > 0 */
+    int32_t head_dim;    /* must be 128 */
+    int32_t io_dtype;    /* KDA_DTYPE_*: q, k, v, g and the conv caches */
+    int32_t out_dtype;   /* KDA_DTYPE_*: o */
+    int32_t prologue;    /* 1: conv4 + SiLU + L2 on q, k (SiLU only on v); 0: q, k, v used as given */
+    int32_t epilogue;    /* 1: o = sigmoid(g) * RMSNorm(o~) * w_rms; 0: o = o~ */
+    int32_t algo;        /* KDA_ALGO_* (prefill only) */
+    float scale;         /* read scale; 1/sqrt(128) in the layer */
+    float l2_eps;        /* x / sqrt(sum x^2 + l2_eps) */
+    float rms_eps;       /* x / sqrt(mean x^2 + rms_eps) */
+} kda_config;
+
+/* Fills *cfg with the layer's defaults for H heads: bf16 io and output,
+ * prologue and epilogue on, AUTO algorithm, scale 1/sqrt(128), eps 1e-6. */
+void kda_config_init(kda_config *cfg, int32_t num_heads);
+
+/* ------------------------------------------------------------------ prefill
+ * Runs the whole layer core over N packed variable-length sequences.
+ * Sequence n covers tokens [cu_seqlens[n], cu_seqlens[n+1]); it starts from
+ * state_in[n] (zeros when NULL) and conv_in[n] (zeros when NULL) and leaves
+ * its final state in state_out[n] and its last three pre-conv inputs in
+ * conv_out[n].  A zero-length sequence copies state and cache through.
+ */
+typedef struct {
+    int32_t num_seqs;             /* N > 0 */
+    const int32_t *cu_seqlens;    /* device [N+1]: cu[0] = 0, non-decreasing, cu[N] = total_tokens */
+    int64_t total_tokens;         /* T >= 0 */
+    const void *q, *k, *v;        /* [T][H][128] io_dtype */
+    const float *log_alpha;       /* [T][H][128] fp32, in [-5, 0] */
+    const float *beta;            /* [T][H] fp32, in [0, 1] */
+    const void *g;                /* [T][H][128] io_dtype; required iff epilogue */
+    const float *conv_w;          /* [3][H*128][4] fp32; required iff prologue */
+    const void *conv_in;          /* [N][3][3][H*128] io_dtype or NULL (zero history) */
+    void *conv_out;               /* same layout or NULL (not written); may alias conv_in */
+    const float *rms_w;           /* [128] fp32 or NULL (ones) */
+    const float *state_in;        /* [N][H][128][128] fp32 or NULL (zeros) */
+    float *state_out;             /* same layout or NULL (not written); may alias state_in */
+    void *o;                      /* [T][H][128] out_dtype; must not alias any input */
+    void *workspace;              /* device scratch of at least kda_prefill_workspace_size bytes */
+    size_t workspace_bytes;
+} kda_prefill_args;
+
+/* Bytes of device workspace kda_prefill needs for N sequences (it holds the
+ * longest-first order of the sequences).  Writes the size to *bytes. */
+kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
+                                      int64_t total_tokens, size_t *bytes);
+
+kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *args, void *hip_stream);
+
+/* -------------------------------------------------------------- decode step
+ * One token per request, the same layer core as prefill at T = 1 per
+ * sequence: the conv caches are shifted and the state is updated in place
+ * ("Kimi K3: Architecture and SGLang Day-0 Support": each step reads and
+ * writes only S, which is overwritten in place).
+ */
+typedef struct {
+    int32_t batch;                /* B > 0 requests */
+    const void *q, *k, *v;        /* [B][H][128] io_dtype */
+    const float *log_alpha;       /* [B][H][128] fp32 */
+    const float *beta;            /* [B][H] fp32 */
+    const void *g;                /* [B][H][128] io_dtype; required iff epilogue */
+    const float *conv_w;          /* [3][H*128][4] fp32; required iff prologue */
+    void *conv_state;             /* [slots][3][3][H*128] io_dtype, updated in place; required iff prologue */
+    const float *rms_w;           /* [128] fp32 or NULL (ones) */
+    float *state;                 /* [slots][H][128][128] fp32, updated in place */
+    const int32_t *slots;         /* device [B] pool slot of each request, or NULL (slot b for request b) */
+    void *o;                      /* [B][H][128] out_dtype */
+} kda_decode_args;
+
+kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *args, void *hip_stream);
+
+/* ------------------------------------------------------------------- misc */
+const char *kda_status_string(kda_status status); /* static string, never NULL */
+uint32_t kda_abi_version(void);                    /* KDA_ABI_VERSION */
+size_t kda_state_bytes(int32_t num_heads);          /* bytes of one sequence's state: H*128*128*4 */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_kda_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = kda.lib()
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_version_and_sizes():
+    assert kda.abi_version() == 1
+    assert kda.state_bytes(96) == 96 * 128 * 128 * 4
+    # the pages' per-request figure: 69 KDA layers x 12 heads per GPU at TP=8 x 128^2 x fp32
+    assert abs(69 * kda.state_bytes(12) / 1e6 - 54.26) < 0.01
+    assert kda.lib().kda_state_bytes(0) == 0
+
+
+def test_status_strings():
+    L = kda.lib()
+    for s in range(5):
+        assert L.kda_status_string(s)
+    assert L.kda_status_string(99) == b"unknown status"
+
+
+def test_config_defaults():
+    c = kda.config(96)
+    assert (c.num_heads, c.head_dim, c.io_dtype, c.out_dtype, c.prologue, c.epilogue, c.algo) == \
+        (96, 128, kda.BF16, kda.BF16, 1, 1, 0)
+    assert abs(c.scale - 128 ** -0.5) < 1e-7 and abs(c.l2_eps - 1e-6) < 1e-12
+
+
+def test_workspace_size():
+    c = kda.config(96)
+    assert kda.workspace_size(c, 1, 100) == 0
+    assert kda.workspace_size(c, 64, 10 ** 6) == 256
+    assert kda.workspace_size(c, 65, 10) == 512
+    with pytest.raises(kda.KdaError):
+        kda.workspace_size(c, 0, 10)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any use
+
+
+def _args(**over):
+    a = kda.PrefillArgs()
+    a.num_seqs, a.cu_seqlens, a.total_tokens = 2, FAKE, 10
+    for f in ("q", "k", "v", "log_alpha", "beta", "g", "conv_w", "o", "state_out"):
+        setattr(a, f, FAKE)
+    a.workspace, a.workspace_bytes = FAKE, 256
+    for k_, v_ in over.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def _prefill(cfg, a):
+    return kda.lib().kda_prefill(ctypes.byref(cfg), ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field", ["cu_seqlens", "q", "k", "v", "log_alpha", "beta", "g", "o", "conv_w"])
+def test_prefill_rejects_null_required(field):
+    # a valid pointer everywhere except one required field, and a deliberately
+    # too-small workspace as a second fault the check must not reach first
+    assert _prefill(kda.config(4), _args(**{field: None})) == kda.ERR_INVALID_ARGUMENT
+
+
+def test_prefill_rejects_misaligned():
+    assert _prefill(kda.config(4), _args(q=FAKE + 2)) == kda.ERR_INVALID_ARGUMENT
+    assert _prefill(kda.config(4), _args(state_in=FAKE + 8)) == kda.ERR_INVALID_ARGUMENT
+
+
+def test_prefill_rejects_bad_config():
+    assert kda.lib().kda_prefill(None, ctypes.byref(_args()), None) == kda.ERR_INVALID_ARGUMENT
+    c = kda.config(4, head_dim=64)
+    assert _prefill(c, _args()) == kda.ERR_UNSUPPORTED
+    for field, val in (("num_heads", 0), ("io_dtype", 7), ("out_dtype", -1), ("prologue", 2),
+                       ("algo", 9)):
+        c = kda.config(4)
+        setattr(c, field, val)
+        assert _prefill(c, _args()) == kda.ERR_INVALID_ARGUMENT, field
+    c = kda.config(4)
+    c.rms_eps = -1.0
+    assert _prefill(c, _args()) == kda.ERR_INVALID_ARGUMENT
+
+
+def test_prefill_rejects_bad_sizes_and_workspace():
+    assert _prefill(kda.config(4), _args(num_seqs=0)) == kda.ERR_INVALID_ARGUMENT
+    assert _prefill(kda.config(4), _args(total_tokens=-1)) == kda.ERR_INVALID_ARGUMENT
+    assert _prefill(kda.config(4), _args(workspace=None)) == kda.ERR_WORKSPACE_TOO_SMALL
+    assert _prefill(kda.config(4), _args(workspace_bytes=8)) == kda.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_optional_pointers_follow_config():
+    # g and conv_w are only required when the epilogue / prologue are on: with both
+    # off a null g / conv_w passes those checks and the call fails on the workspace
+    c = kda.config(4, prologue=False, epilogue=False)
+    assert _prefill(c, _args(g=None, conv_w=None, workspace=None)) == kda.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_decode_rejects_bad_arguments():
+    L = kda.lib()
+
+    def dec(cfg, **over):
+        a = kda.DecodeArgs()
+        a.batch = 4
+        for f in ("q", "k", "v", "log_alpha", "beta", "g", "conv_w", "conv_state", "state", "o"):
+            setattr(a, f, FAKE)
+        for k_, v_ in over.items():
+            setattr(a, k_, v_)
+        return L.kda_decode_step(ctypes.byref(cfg), ctypes.byref(a), None)
+
+    for f in ("q", "k", "v", "log_alpha", "beta", "g", "conv_w", "conv_state", "state", "o"):
+        assert dec(kda.config(4), **{f: None}) == kda.ERR_INVALID_ARGUMENT, f
+    assert dec(kda.config(4), batch=0) == kda.ERR_INVALID_ARGUMENT
+    assert dec(kda.config(4), slots=FAKE + 4) == kda.ERR_INVALID_ARGUMENT
+    assert dec(kda.config(4, head_dim=256)) == kda.ERR_UNSUPPORTED

@@ -26,7 +26,9 @@ Workloads (H heads of width d = 128):
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence
 
 import numpy as np
@@ -38,11 +40,19 @@ T_Q, T_K, T_V, T_G, T_ALPHA, T_BETA, T_CONVW, T_CONVIN, T_STATE, T_LENS = range(
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bf16 (ties to even); returns float32."""
-    a = np.ascontiguousarray(x, dtype=np.float32)
-    u = a.view(np.uint32)
-    r = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32)
+    """Round finite float32 values to the nearest bf16 (ties to even); returns a new
+    float32 array.  (Finite inputs only: u + 0x8000 cannot wrap below the NaN range.)"""
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32)
+
+
+def _workers() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        return 4
 
 
 def _rng(seed: int, tensor: int, n: int = 0, h: int = 0) -> np.random.Generator:
@@ -68,15 +78,35 @@ class PrefillSpec:
         return int(np.sum(self.lens))
 
 
-def _fill_blocks(out: np.ndarray, seed: int, tensor: int, cu: np.ndarray, draw) -> None:
+def _fill_blocks(out: np.ndarray, seed: int, tensor: int, cu: np.ndarray, draw,
+                 bf16: bool = False) -> None:
+    """out[cu[n]:cu[n+1], h] for every (sequence n, head h) from its own generator,
+    rounded to bf16 values when asked.  Workers write their rows directly."""
     N = len(cu) - 1
     H = out.shape[1]
-    for n in range(N):
+    jobs = [(n, h) for n in range(N) for h in range(H) if cu[n + 1] > cu[n]]
+
+    def one(job):
+        n, h = job
         s, e = int(cu[n]), int(cu[n + 1])
-        if e == s:
-            continue
-        for h in range(H):
-            out[s:e, h] = draw(_rng(seed, tensor, n, h), (e - s,) + out.shape[2:])
+        blk = draw(_rng(seed, tensor, n, h), (e - s,) + out.shape[2:])
+        if bf16:
+            blk = _bf16_inplace(blk)
+        out[s:e, h] = blk
+
+    if out.size >= 1 << 16:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(one, jobs))
+    else:
+        for j in jobs:
+            one(j)
+
+
+def _bf16_inplace(a: np.ndarray) -> np.ndarray:
+    u = a.view(np.uint32)
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    u &= np.uint32(0xFFFF0000)
+    return a
 
 
 def _normal32(rng, shape):
@@ -122,11 +152,11 @@ def gen_prefill(spec: PrefillSpec) -> Dict[str, np.ndarray]:
     for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V)):
         a = np.empty((T, H, D), np.float32)
         draw = _unit if (spec.unit_qk and name != "v") else _normal32
-        _fill_blocks(a, sd, tid, cu, draw)
+        _fill_blocks(a, sd, tid, cu, draw, bf16=spec.io == "bf16")
         out[name] = a
     if spec.epilogue:
         a = np.empty((T, H, D), np.float32)
-        _fill_blocks(a, sd, T_G, cu, _normal32)
+        _fill_blocks(a, sd, T_G, cu, _normal32, bf16=spec.io == "bf16")
         out["g"] = a
     a = np.empty((T, H, D), np.float32)
     _fill_blocks(a, sd, T_ALPHA, cu, _log_alpha(spec.decay))
@@ -143,14 +173,16 @@ def gen_prefill(spec: PrefillSpec) -> Dict[str, np.ndarray]:
             out["conv_in"] = ci
     if spec.state_std is not None:
         st = np.empty((N, H, D, D), np.float32)
-        for n in range(N):
-            for h in range(H):
-                st[n, h] = _rng(sd, T_STATE, n, h).standard_normal((D, D)) * spec.state_std
+
+        def one(nh):
+            n, h = nh
+            st[n, h] = _rng(sd, T_STATE, n, h).standard_normal((D, D)) * spec.state_std
+
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(one, [(n, h) for n in range(N) for h in range(H)]))
         out["state_in"] = st
-    if spec.io == "bf16":
-        for key in ("q", "k", "v", "g", "conv_in"):
-            if key in out:
-                out[key] = bf16_round(out[key])
+    if spec.io == "bf16" and "conv_in" in out:
+        out["conv_in"] = bf16_round(out["conv_in"])
     return out
 
 
@@ -173,7 +205,7 @@ def gen_decode(spec: DecodeSpec) -> Dict[str, np.ndarray]:
     out: Dict[str, np.ndarray] = {}
     for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V), ("g", T_G)):
         a = np.empty((B, H, D), np.float32)
-        _fill_blocks(a, sd, tid, cu, _normal32)
+        _fill_blocks(a, sd, tid, cu, _normal32, bf16=spec.io == "bf16")
         out[name] = a
     a = np.empty((B, H, D), np.float32)
     _fill_blocks(a, sd, T_ALPHA, cu, _log_alpha(spec.decay))
@@ -187,13 +219,16 @@ def gen_decode(spec: DecodeSpec) -> Dict[str, np.ndarray]:
         cs[n] = _rng(sd, T_CONVIN, n).standard_normal((3, 3, H * D), dtype=np.float32)
     out["conv_state"] = cs
     st = np.empty((B, H, D, D), np.float32)
-    for n in range(B):
-        rng = _rng(sd, T_STATE, n)
-        st[n] = rng.standard_normal((H, D, D), dtype=np.float32) * np.float32(spec.state_std)
+
+    def one(n):
+        st[n] = _rng(sd, T_STATE, n).standard_normal((H, D, D), dtype=np.float32)
+        st[n] *= np.float32(spec.state_std)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(B)))
     out["state"] = st
     if spec.io == "bf16":
-        for key in ("q", "k", "v", "g", "conv_state"):
-            out[key] = bf16_round(out[key])
+        out["conv_state"] = bf16_round(out["conv_state"])
     return out
 
 

@@ -1,0 +1,241 @@
+"""Benchmark of the KDA layer core on one MI355X.
+
+One step is one pass of the whole hot path: a full-layer prefill (conv4 +
+SiLU + L2 prologue, chunked recurrence, sigma(g) * RMSNorm epilogue) over
+4 sequences x 4096 tokens x 96 heads (bf16 q, k, v, g; fp32 gates; S0 = 0),
+followed by one decode step for 256 requests x 96 heads that updates a
+[256, 96, 128, 128] fp32 state in place.
+
+Printed (one JSON line): prefill tokens/s as `value`, decode state GB/s
+(2 * B * H * 128^2 * 4 bytes per step / step time) beside it, a roofline
+entry for each kernel (algorithmic bytes per launch / mean launch time, from
+HIP events on the launch stream), and the fp64 CPU oracle timed on one
+sequence of the same workload on the host's cores.
+
+    python bench.py [--steps K] [--warmup W] [--algo auto|chunked|recurrent]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA
+D = 128
+
+
+def prefill_algorithmic_bytes(T: int, H: int, N: int) -> int:
+    """Bytes the prefill must move: per token-head q, k, v, g (bf16, 4 x 256 B),
+    log alpha (fp32, 512 B), beta (4 B) and o (bf16, 256 B) = 1796 B; per
+    (sequence, head) the 64 KiB fp32 final state; the fp32 conv weights
+    (3 x H*128 x 4) and the bf16 conv cache out (N x 3 x 3 x H*128)."""
+    per_token_head = 4 * 2 * D + 4 * D + 4 + 2 * D
+    return (T * H * per_token_head + N * H * D * D * 4 + 3 * H * D * 4 * 4 +
+            N * 9 * H * D * 2)
+
+
+def decode_algorithmic_bytes(B: int, H: int) -> int:
+    """Bytes one decode step must move: the fp32 state read and written
+    (2 x 64 KiB per (request, head)), q, k, v, g in and o out (bf16), log alpha
+    (fp32) and beta, the conv cache read and written (bf16, 3 x 3 x H*128 per
+    request) and the conv weights."""
+    state = 2 * B * H * D * D * 4
+    act = B * H * (5 * D * 2 + D * 4 + 4)
+    conv = 2 * B * 9 * H * D * 2 + 3 * H * D * 4 * 4
+    return state + act + conv
+
+
+def prefill_mfma_flops(T: int, H: int) -> int:
+    """Algorithmic MFMA flops of the chunked prefill at 64-token chunks with
+    16-token triangle granularity: 6 d^2 + 5 (C + 16) d per token-head."""
+    return T * H * (6 * D * D + 5 * (64 + 16) * D)
+
+
+def cpu_info() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_events(fn, steps: int, stream):
+    """Mean ms of fn() over `steps` calls, from HIP events recorded on `stream`."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(ts)), float(np.median(ts))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "recurrent"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the KDA core shards by head and by request with no "
+              f"collective inside it, and this build runs on a single MI355X; --gpus {args.gpus} "
+              f"is not supported.", file=sys.stderr)
+        return 2
+
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    import kda_workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- prefill inputs
+    spec = W.workload("prefill_4x4096")
+    t0 = time.perf_counter()
+    x = W.gen_prefill(spec)
+    log(f"generated prefill inputs in {time.perf_counter() - t0:.1f}s")
+    T, H, N = spec.total, spec.heads, len(spec.lens)
+
+    def dev_t(a, dt):
+        return torch.from_numpy(a).to(dev).to(dt)
+
+    q, k, v, g = (dev_t(x[n], bf) for n in ("q", "k", "v", "g"))
+    la = dev_t(x["log_alpha"], torch.float32)
+    beta = dev_t(x["beta"], torch.float32)
+    cw = dev_t(x["conv_w"], torch.float32)
+    cu = dev_t(x["cu_seqlens"], torch.int32)
+    cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", prologue=True, epilogue=True,
+                     algo=args.algo)
+    o = torch.empty((T, H, D), dtype=bf, device=dev)
+    s_out = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    c_out = torch.empty((N, 3, 3, H * D), dtype=bf, device=dev)
+    ws_n = kda.workspace_size(cfg, N, T)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run_prefill():
+        kda.prefill(q, k, v, la, beta, cu, g=g, conv_w=cw, o=o, state_out=s_out, conv_out=c_out,
+                    workspace=ws if ws_n else None, cfg=cfg, stream=stream)
+
+    # ---------------------------------------------------------------- decode inputs
+    dspec = W.workload("decode_256")
+    t0 = time.perf_counter()
+    y = W.gen_decode(dspec)
+    log(f"generated decode inputs in {time.perf_counter() - t0:.1f}s")
+    B = dspec.batch
+    dq, dk_, dv_, dg = (dev_t(y[n], bf) for n in ("q", "k", "v", "g"))
+    dla = dev_t(y["log_alpha"], torch.float32)
+    dbeta = dev_t(y["beta"], torch.float32)
+    dcw = dev_t(y["conv_w"], torch.float32)
+    dstate = dev_t(y["state"], torch.float32)
+    dconv = dev_t(y["conv_state"], bf)
+    del y
+    dcfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", prologue=True, epilogue=True)
+    do = torch.empty((B, H, D), dtype=bf, device=dev)
+
+    def run_decode():
+        kda.decode_step(dq, dk_, dv_, dla, dbeta, dstate, g=dg, conv_w=dcw, conv_state=dconv,
+                        o=do, cfg=dcfg, stream=stream)
+
+    # ---------------------------------------------------------------- timing
+    for _ in range(args.warmup):
+        run_prefill()
+        run_decode()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    t_wall0 = time.perf_counter()
+    pre_mean, pre_med = time_events(run_prefill, args.steps, stream)
+    dec_mean, dec_med = time_events(run_decode, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    log(f"prefill {pre_mean:.3f} ms (median {pre_med:.3f}); decode {dec_mean:.4f} ms "
+        f"(median {dec_med:.4f}); wall {wall:.2f}s")
+
+    tok_s = T / (pre_mean * 1e-3)
+    pb = prefill_algorithmic_bytes(T, H, N)
+    pf = prefill_mfma_flops(T, H)
+    pre_gbps = pb / (pre_mean * 1e-3) / 1e9
+    db = decode_algorithmic_bytes(B, H)
+    state_bytes = 2 * B * H * D * D * 4
+    dec_state_gbps = state_bytes / (dec_mean * 1e-3) / 1e9
+    dec_gbps = db / (dec_mean * 1e-3) / 1e9
+    algo_name = {0: "auto", 1: "recurrent", 2: "chunked"}[cfg.algo]
+    if algo_name == "auto":
+        algo_name = kda.resolved_algo(cfg)
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        L0 = int(spec.lens[0])
+        sub = {n: x[n][:L0] for n in ("q", "k", "v", "g", "log_alpha", "beta")}
+        t0 = time.perf_counter()
+        oracle.prefill(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"], [0, L0],
+                       g=sub["g"], conv_w=x["conv_w"], threads=threads)
+        ct = time.perf_counter() - t0
+        cpu = {"value": L0 / ct, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"sequence 0 of the prefill workload: {L0} tokens x {H} heads, full layer, "
+                         f"fp64, {ct:.1f}s wall on {threads} threads ({cpu_info()})"}
+        log(f"oracle: {L0} tokens x {H} heads in {ct:.1f}s on {threads} threads")
+
+    res = {
+        "metric": "KDA prefill tokens/sec (H=96,d=128) + decode state GB/s at B=256",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre_mean + dec_mean,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill B=4 x T=4096, H=96, d=128, full layer (conv4+SiLU+L2, "
+                               "sigma(g)*RMSNorm), bf16 io, fp32 gates and state; decode B=256, H=96",
+                   "prefill_algo": algo_name, "global_batch": N, "seq_len": spec.lens[0],
+                   "heads": H, "head_dim": D, "decode_batch": B},
+        "prefill": {"ms": pre_mean, "ms_median": pre_med, "tokens_per_s": tok_s,
+                    "algorithmic_bytes": pb, "mfma_flops": pf,
+                    "mfma_tflops": pf / (pre_mean * 1e-3) / 1e12,
+                    "mfma_frac_of_peak": pf / (pre_mean * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                    "hbm_roofline_tokens_per_s": T / (pb / (HBM_PEAK_GBPS * 1e9))},
+        "decode": {"ms": dec_mean, "ms_median": dec_med, "state_GBps": dec_state_gbps,
+                   "algorithmic_bytes": db, "GBps": dec_gbps,
+                   "frac_of_hbm_peak": dec_gbps / HBM_PEAK_GBPS},
+        "roofline": {"kernel": f"prefill ({algo_name})", "bound": "hbm", "achieved": pre_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": pre_gbps / HBM_PEAK_GBPS,
+                     "traffic": None},
+        "roofline_decode": {"kernel": "decode step", "bound": "hbm", "achieved": dec_gbps,
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dec_gbps / HBM_PEAK_GBPS,
+                            "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -26,7 +26,8 @@ F32, BF16 = 0, 1
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 
-EXPORTS = ("kda_config_init", "kda_prefill_workspace_size", "kda_prefill", "kda_decode_step",
+EXPORTS = ("kda_config_init", "kda_prefill_workspace_size", "kda_prefill",
+           "kda_prefill_resolved_algo", "kda_decode_step",
            "kda_status_string", "kda_abi_version", "kda_state_bytes")
 
 
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill_workspace_size.restype = ctypes.c_int32
         L.kda_prefill.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(PrefillArgs), _vp]
         L.kda_prefill.restype = ctypes.c_int32
+        L.kda_prefill_resolved_algo.argtypes = [ctypes.POINTER(Config)]
+        L.kda_prefill_resolved_algo.restype = ctypes.c_int32
         L.kda_decode_step.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(DecodeArgs), _vp]
         L.kda_decode_step.restype = ctypes.c_int32
         L.kda_status_string.argtypes = [ctypes.c_int32]
@@ -249,6 +252,14 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
     a.state, a.slots, a.o = _ptr(state), _ptr(slots), _ptr(o)
     _check(lib().kda_decode_step(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
     return o
+
+
+def resolved_algo(cfg: Config) -> str:
+    """Name of the prefill algorithm the library runs for `cfg` (AUTO resolved)."""
+    code = lib().kda_prefill_resolved_algo(ctypes.byref(cfg))
+    if code < 0:
+        raise KdaError(ERR_INVALID_ARGUMENT, "invalid configuration")
+    return {v: k for k, v in ALGOS.items()}[code]
 
 
 def abi_version() -> int:

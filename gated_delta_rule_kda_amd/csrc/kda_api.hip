@@ -98,6 +98,12 @@ void kda_config_init(kda_config *cfg, int32_t num_heads) {
     cfg->rms_eps = 1e-6f;
 }
 
+int32_t kda_prefill_resolved_algo(const kda_config *cfg) {
+    if (check_config(cfg) != KDA_OK) return -1;
+    if (cfg->algo != KDA_ALGO_AUTO) return cfg->algo;
+    return KDA_ALGO_RECURRENT;
+}
+
 kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens,
                                       size_t *bytes) {
     kda_status st = check_config(cfg);
@@ -124,8 +130,7 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     const size_t need = order_workspace_bytes(a->num_seqs);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
 
-    int algo = cfg->algo;
-    if (algo == KDA_ALGO_AUTO) algo = cfg->io_dtype == KDA_DTYPE_BF16 ? KDA_ALGO_CHUNKED : KDA_ALGO_RECURRENT;
+    const int algo = kda_prefill_resolved_algo(cfg);
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     int32_t *order = need > 0 ? static_cast<int32_t *>(a->workspace) : nullptr;

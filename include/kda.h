@@ -122,6 +122,10 @@ kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
 
 kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *args, void *hip_stream);
 
+/* The KDA_ALGO_* that kda_prefill runs for this configuration (AUTO resolved),
+ * or -1 when the configuration is invalid.  Host only; enqueues nothing. */
+int32_t kda_prefill_resolved_algo(const kda_config *cfg);
+
 /* -------------------------------------------------------------- decode step
  * One token per request, the same layer core as prefill at T = 1 per
  * sequence: the conv caches are shifted and the state is updated in place

@@ -79,16 +79,23 @@ class PrefillSpec:
 
 
 def _fill_blocks(out: np.ndarray, seed: int, tensor: int, cu: np.ndarray, draw,
-                 bf16: bool = False) -> None:
-    """out[cu[n]:cu[n+1], h] for every (sequence n, head h) from its own generator,
-    rounded to bf16 values when asked.  Workers write their rows directly."""
+                 bf16: bool = False, per_head: bool = True) -> None:
+    """out[cu[n]:cu[n+1], h] for every (sequence n, head h) from its own generator
+    (or out[cu[n]:cu[n+1]] for every sequence n from one generator when
+    per_head is False), rounded to bf16 values when asked.  Workers write
+    their rows directly."""
     N = len(cu) - 1
     H = out.shape[1]
-    jobs = [(n, h) for n in range(N) for h in range(H) if cu[n + 1] > cu[n]]
+    heads = range(H) if per_head else [None]
+    jobs = [(n, h) for n in range(N) for h in heads if cu[n + 1] > cu[n]]
 
     def one(job):
         n, h = job
         s, e = int(cu[n]), int(cu[n + 1])
+        if h is None:
+            blk = draw(_rng(seed, tensor, n, H), (e - s,) + out.shape[1:])
+            out[s:e] = _bf16_inplace(blk) if bf16 else blk
+            return
         blk = draw(_rng(seed, tensor, n, h), (e - s,) + out.shape[2:])
         if bf16:
             blk = _bf16_inplace(blk)
@@ -203,32 +210,30 @@ def gen_decode(spec: DecodeSpec) -> Dict[str, np.ndarray]:
     B, H, sd = spec.batch, spec.heads, spec.seed
     cu = np.arange(B + 1, dtype=np.int64)
     out: Dict[str, np.ndarray] = {}
+    # one generator per request (all heads at once)
     for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V), ("g", T_G)):
         a = np.empty((B, H, D), np.float32)
-        _fill_blocks(a, sd, tid, cu, _normal32, bf16=spec.io == "bf16")
+        _fill_blocks(a, sd, tid, cu, _normal32, bf16=spec.io == "bf16", per_head=False)
         out[name] = a
     a = np.empty((B, H, D), np.float32)
-    _fill_blocks(a, sd, T_ALPHA, cu, _log_alpha(spec.decay))
+    _fill_blocks(a, sd, T_ALPHA, cu, _log_alpha(spec.decay), per_head=False)
     out["log_alpha"] = a
     b = np.empty((B, H), np.float32)
-    _fill_blocks(b, sd, T_BETA, cu, _beta)
+    _fill_blocks(b, sd, T_BETA, cu, _beta, per_head=False)
     out["beta"] = b
     out["conv_w"] = (_rng(sd, T_CONVW).standard_normal((3, H * D, 4)) * 0.5).astype(np.float32)
     cs = np.empty((B, 3, 3, H * D), np.float32)
-    for n in range(B):
-        cs[n] = _rng(sd, T_CONVIN, n).standard_normal((3, 3, H * D), dtype=np.float32)
-    out["conv_state"] = cs
     st = np.empty((B, H, D, D), np.float32)
 
     def one(n):
-        st[n] = _rng(sd, T_STATE, n).standard_normal((H, D, D), dtype=np.float32)
+        cs[n] = _rng(sd, T_CONVIN, n).standard_normal((3, 3, H * D), dtype=np.float32)
+        _rng(sd, T_STATE, n).standard_normal((H, D, D), dtype=np.float32, out=st[n])
         st[n] *= np.float32(spec.state_std)
 
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(one, range(B)))
     out["state"] = st
-    if spec.io == "bf16":
-        out["conv_state"] = bf16_round(out["conv_state"])
+    out["conv_state"] = bf16_round(cs) if spec.io == "bf16" else cs
     return out
 
 

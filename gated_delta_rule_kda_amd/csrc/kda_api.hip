@@ -101,7 +101,7 @@ void kda_config_init(kda_config *cfg, int32_t num_heads) {
 int32_t kda_prefill_resolved_algo(const kda_config *cfg) {
     if (check_config(cfg) != KDA_OK) return -1;
     if (cfg->algo != KDA_ALGO_AUTO) return cfg->algo;
-    return KDA_ALGO_RECURRENT;
+    return cfg->io_dtype == KDA_DTYPE_BF16 ? KDA_ALGO_CHUNKED : KDA_ALGO_RECURRENT;
 }
 
 kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens,

@@ -2,9 +2,9 @@
 //
 // The per-token recurrence of the "Kimi K3 - KDA layer" step list
 // (S <- Diag(alpha) S;  S <- S + beta k (v - S^T k)^T;  o~ = S^T q / sqrt(128))
-// is regrouped over chunks of C = 32 tokens.  For one chunk entering with
-// state S0, with G the running sum of log alpha from the chunk start
-// (per key channel) and Gamma = e^G:
+// is regrouped over chunks of C = 16 tokens.  For one chunk entering with
+// state S0, with G the running sum of log alpha from the chunk start (per
+// key channel), Gamma = e^G and G_C its value at the last token:
 //
 //   A[s][j] = beta_s sum_c k_s[c] k_j[c] e^{G_s[c] - G_j[c]}      (j < s)
 //   P[r][j] =        sum_c q_r[c] k_j[c] e^{G_r[c] - G_j[c]}      (j <= r)
@@ -13,22 +13,27 @@
 //   O       = scale (Qbar S0 + P U),      Qbar = Gamma (.) Q
 //   S1      = Diag(Gamma_C) S0 + Khat^T U, Khat = e^{G_C - G} (.) K
 //
-// which is the recurrence unrolled over the chunk (u_r = beta_r (v_r -
-// (Diag(alpha_r) S_{r-1})^T k_r) is the per-token correction; stacking the
-// u_r gives the unit-lower triangular system (I + A) U = Diag(beta)(V -
-// Kbar S0)).  The decay factors are kept finite by the 16-token sub-tile
-// references of "Kimi K3's Architecture ..." (section "Channel-wise decay,
-// and the floor K3 puts under it"): within a sub-tile the factors are taken
-// relative to the sub-tile start, so no factor exceeds e^{5*16} = e^80.
+// which is the recurrence unrolled over the chunk: u_r = beta_r (v_r -
+// (Diag(alpha_r) S_{r-1})^T k_r) is the per-token correction, and stacking
+// the u_r gives the unit-lower triangular system (I + A) U = Diag(beta)(V -
+// Kbar S0).  The Gram blocks use the factorisation e^{G_s - G_j} =
+// e^{G_s} e^{-G_j} within the chunk; at the log-decay floor of -5 per token
+// ("Kimi K3's Architecture ...", section "Channel-wise decay, and the floor
+// K3 puts under it") a 16-token chunk keeps e^{-G} <= e^80, inside the fp32 /
+// bf16 exponent range.
 //
-// Layout of the work: one workgroup of 8 waves per (sequence, head), looping
-// over the sequence's chunks.  Wave w owns value columns 16w .. 16w+15 of S
-// and keeps that 128x16 fp32 slice in registers, in the accumulator layout
-// of v_mfma_f32_16x16x32_bf16 (lane l holds rows 16t + 4(l/16) + i, column
-// l%16).  The contractions that touch S, U or X take that layout directly
-// as their B operand: the 32 K-slots of one MFMA read rows pi(8h+i) =
-// 16(i/4) + 4h + (i%4) of two stacked accumulator tiles, so the A operands
-// (staged in LDS) store their K index in the same permuted order.
+// Work layout: one workgroup of 4 waves per (sequence, head), walking the
+// sequence's chunks; about 64 KB of LDS, so two workgroups share a CU and
+// hide each other's latencies.  Wave w owns value columns 32w .. 32w+31 of S
+// and keeps that 128 x 32 fp32 slice in registers, in the accumulator layout
+// of the 16x16 MFMAs (lane l holds rows 16t + 4(l/16) + i, column l%16 of
+// each 16-column tile).  Contractions over the 16 tokens of a chunk
+// (v_mfma_f32_16x16x16_bf16) take accumulator tiles directly as their B
+// operand.  Contractions over the 128 key channels (v_mfma_f32_16x16x32_bf16)
+// read S from the same registers: K slot 8h + i of a 32-channel step holds
+// channel 16(i/4) + 4h + (i%4), so the channel-indexed operands in LDS store
+// their channels in that permuted order (the Gram products contract two such
+// operands, which the permutation leaves unchanged).
 //
 // Precision: every contraction splits both operands into bf16 hi + lo parts
 // and sums hi*hi + hi*lo + lo*hi in fp32 (three MFMAs), which keeps each
@@ -38,53 +43,50 @@
 namespace kda {
 namespace {
 
-constexpr int C = 32;          // tokens per chunk
-constexpr int SUBT = 16;       // decay sub-tile
-constexpr int NW = 8;          // waves per workgroup
+constexpr int C = 16;          // tokens per chunk
+constexpr int NW = 4;          // waves per workgroup
 constexpr int THREADS = NW * 64;
-constexpr int OPK = D + 8;     // padded row (bf16 elements) of [*][128] operand planes
-constexpr int OPT = C + 8;     // padded row of [*][32] operand planes
-constexpr int FPK = D + 4;     // padded row (floats) of [32][128] fp32 buffers
+constexpr int OPK = D + 8;     // padded row (bf16 elements) of [16][128] operand planes
+constexpr int OPT = C + 4;     // padded row of [*][16] operand planes
+constexpr int FPK = D + 4;     // padded row (floats) of [16][128] fp32 tiles
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// ------------------------------------------------------------------ LDS map
-// Byte offsets inside one dynamic-size-free static buffer.  The "gram"
-// region holds the Gram-matrix operands until the Gram products are done,
-// then the fp32 V tile (at +0) and the fp32 output staging tile (at +QL).
-constexpr int PL_C_D = C * OPK;          // bf16 elements of one [32][128] plane
-constexpr int PL_S_D = SUBT * OPK;       // one [16][128] plane
-constexpr int PL_D_C = D * OPT;          // one [128][32] plane
-constexpr int PL_C_C = C * OPT;          // one [32][32] plane
+// ------------------------------------------------------------------ LDS map (bytes)
+constexpr int PL_CD = C * OPK;           // bf16 elements of one [16][128] plane
+constexpr int PL_DC = D * OPT;           // one [128][16] plane
+constexpr int PL_CC = C * OPT;           // one [16][16] plane
 
-constexpr int OFF_KL = 0;                                  // kl = k^ e^{G-R}        hi,lo [32][136]
-constexpr int OFF_QL = OFF_KL + 2 * PL_C_D * 2;            // ql = q^ e^{G-R}        hi,lo
-constexpr int OFF_KRD = OFF_QL + 2 * PL_C_D * 2;           // krd = k^ e^{R-G}       hi,lo
-constexpr int OFF_KR10 = OFF_KRD + 2 * PL_C_D * 2;         // k^ e^{R1-G}, sub-tile 0 hi,lo [16][136]
-constexpr int OFF_GRAM_END = OFF_KR10 + 2 * PL_S_D * 2;
-constexpr int OFF_V = OFF_KL;                              // fp32 [32][132] (after the Gram products)
-constexpr int OFF_O = OFF_QL;                              // fp32 [32][132] (output staging)
-constexpr int OFF_KBN = OFF_GRAM_END;                      // -Kbar, K-permuted       hi,lo [32][136]
-constexpr int OFF_QB = OFF_KBN + 2 * PL_C_D * 2;           // Qbar, K-permuted        hi,lo [32][136]
-constexpr int OFF_KHT = OFF_QB + 2 * PL_C_D * 2;           // Khat^T, K-permuted      hi,lo [128][40]
-constexpr int OFF_LA = OFF_KHT + 2 * PL_D_C * 2;           // log alpha -> local cumsum fp32 [32][128]
-constexpr int OFF_AF = OFF_LA + C * D * 4;                 // A (beta-scaled) fp32 [32][33]
-constexpr int OFF_TS = OFF_AF + C * 33 * 4;                // D0^-1, D1^-1, Z fp32 [3][16][17]
-constexpr int OFF_PM = OFF_TS + 3 * 16 * 17 * 4;           // P, K-permuted           hi,lo [32][40]
-constexpr int OFF_TM = OFF_PM + 2 * PL_C_C * 2;            // T, K-permuted           hi,lo [32][40]
-constexpr int OFF_BETA = OFF_TM + 2 * PL_C_C * 2;          // fp32 [32]
-constexpr int OFF_ER1 = OFF_BETA + C * 4;                  // e^{R1}  = e^{G at token 15}     [128]
-constexpr int OFF_ET1 = OFF_ER1 + D * 4;                   // e^{G_C - R1}                    [128]
-constexpr int OFF_EGC = OFF_ET1 + D * 4;                   // e^{G_C}                          [128]
-constexpr int OFF_CW = OFF_EGC + D * 4;                    // conv weights fp32 [3][128][4]
-constexpr int OFF_RW = OFF_CW + 3 * D * 4 * 4;             // rms gain fp32 [128]
-constexpr int LDS_BYTES = OFF_RW + D * 4;
+constexpr int OFF_KL = 0;                          // k^ Gamma (= Kbar), channel-permuted      hi,lo
+constexpr int OFF_QL = OFF_KL + 2 * PL_CD * 2;     // q^ Gamma (= Qbar), channel-permuted      hi,lo
+constexpr int OFF_KRD = OFF_QL + 2 * PL_CD * 2;    // k^ / Gamma, channel-permuted             hi,lo
+constexpr int OFF_O = OFF_KRD;                     // fp32 [16][132] output staging (after the Gram)
+constexpr int OFF_KHT = OFF_KRD + 2 * PL_CD * 2;   // Khat^T [channel][token], swizzled        hi,lo
+constexpr int OFF_V = OFF_KHT + 2 * PL_DC * 2;     // fp32 [16][132]
+constexpr int OFF_LA = OFF_V + C * FPK * 4;        // log alpha -> cumulative, fp32 [16][128]
+constexpr int OFF_AF = OFF_LA + C * D * 4;         // A (beta-scaled) fp32 [16][17]
+constexpr int OFF_PM = OFF_AF + C * 17 * 4;        // P                                        hi,lo [16][20]
+constexpr int OFF_TM = OFF_PM + 2 * PL_CC * 2;     // T                                        hi,lo [16][20]
+constexpr int OFF_BETA = OFF_TM + 2 * PL_CC * 2;   // fp32 [16]
+constexpr int OFF_EGC = OFF_BETA + C * 4;          // e^{G_C} fp32 [128]
+constexpr int OFF_CW = OFF_EGC + D * 4;            // conv weights fp32 [3 streams][4 taps][128]
+constexpr int OFF_RW = OFF_CW + 3 * 4 * D * 4;     // rms gain fp32 [128]
+constexpr int OFF_RAW = OFF_RW + D * 4;           // raw q, k, v rows of the chunk [3][16][128] io
+// ... then the last three raw rows of the previous chunks, double-buffered [2][3][3][128] io
+template <typename IO> struct RawLds {
+    static constexpr int CUR = OFF_RAW;
+    static constexpr int HIST = CUR + 3 * C * D * static_cast<int>(sizeof(IO));
+    static constexpr int BYTES = HIST + 2 * 3 * CONV_HIST * D * static_cast<int>(sizeof(IO));
+};
 
-static_assert(C * FPK * 4 <= 2 * PL_C_D * 2, "V / O staging must fit in one operand slot");
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+static_assert(C * FPK * 4 <= 2 * PL_CD * 2, "output staging must fit in the KRD slot");
+static_assert(2 * RawLds<uint16_t>::BYTES <= 160 * 1024, "two bf16-io workgroups per gfx950 CU");
+static_assert(RawLds<float>::BYTES <= 160 * 1024, "one fp32-io workgroup per gfx950 CU");
 
 // Position of K index j (0..31) inside a 32-wide K block of an A operand
 // whose B operand comes from two stacked accumulator tiles: B slot 8h + i
@@ -117,6 +119,33 @@ __device__ __forceinline__ void split1(float a, uint16_t &hi, uint16_t &lo) {
     lo = static_cast<uint16_t>(l);
 }
 
+__device__ __forceinline__ void split4(const float *x, uint2 &hi, uint2 &lo) {
+    split2(x[0], x[1], hi.x, lo.x);
+    split2(x[2], x[3], hi.y, lo.y);
+}
+
+__device__ __forceinline__ f32x4_t mma16(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a),
+                                                     __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
+}
+
+// (a_hi + a_lo)(b_hi + b_lo) without the lo*lo term, K = 16.
+__device__ __forceinline__ f32x4_t mma16_3(uint2 ahi, uint2 alo, uint2 bhi, uint2 blo, f32x4_t c) {
+    c = mma16(alo, bhi, c);
+    c = mma16(ahi, blo, c);
+    return mma16(ahi, bhi, c);
+}
+
+// d = x y for 16x16 fp32 matrices held as (a form of x, b form of y), through
+// bf16 hi/lo operand splits on a fresh accumulator.
+__device__ __forceinline__ void mm16(const float *xa, const float *yb, float *d) {
+    uint2 ah, al, bh, bl;
+    split4(xa, ah, al);
+    split4(yb, bh, bl);
+    const f32x4_t r = mma16_3(ah, al, bh, bl, f32x4_t{0.f, 0.f, 0.f, 0.f});
+    d[0] = r[0]; d[1] = r[1]; d[2] = r[2]; d[3] = r[3];
+}
+
 __device__ __forceinline__ f32x4_t mma(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -136,18 +165,24 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-// Eight consecutive io values starting at element i (i a multiple of 8).
+// Eight consecutive io values starting at element i (i a multiple of 8): a raw
+// 16- or 32-byte load, and its conversion to fp32, kept apart so that a batch
+// of loads can be issued before any of them is consumed.
 template <typename IO> struct Vec8;
 template <> struct Vec8<uint16_t> {
-    static __device__ __forceinline__ void load(const void *p, size_t i, float *x) {
-        uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + i);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    struct Raw { uint4 u; };
+    static __device__ __forceinline__ Raw raw(const void *p, size_t i) {
+        return Raw{*reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + i)};
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *x) {
+        const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             x[2 * e] = __uint_as_float(w[e] << 16);
             x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
         }
     }
+    static __device__ __forceinline__ void load(const void *p, size_t i, float *x) { unpack(raw(p, i), x); }
     static __device__ __forceinline__ void store(void *p, size_t i, const float *x) {
         uint32_t w[4];
 #pragma unroll
@@ -156,54 +191,82 @@ template <> struct Vec8<uint16_t> {
                    (static_cast<uint32_t>(f32_to_bf16(x[2 * e + 1])) << 16);
         *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p) + i) = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    static __device__ __forceinline__ void copy(const void *src, size_t i, void *dst, size_t j) {
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(dst) + j) =
-            *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src) + i);
-    }
 };
 template <> struct Vec8<float> {
-    static __device__ __forceinline__ void load(const void *p, size_t i, float *x) {
+    struct Raw { float4 a, b; };
+    static __device__ __forceinline__ Raw raw(const void *p, size_t i) {
         const float4 *q = reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
-        float4 a = q[0], b = q[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        return Raw{q[0], q[1]};
     }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *x) {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+    }
+    static __device__ __forceinline__ void load(const void *p, size_t i, float *x) { unpack(raw(p, i), x); }
     static __device__ __forceinline__ void store(void *p, size_t i, const float *x) {
         float4 *q = reinterpret_cast<float4 *>(static_cast<float *>(p) + i);
         q[0] = make_float4(x[0], x[1], x[2], x[3]);
         q[1] = make_float4(x[4], x[5], x[6], x[7]);
     }
-    static __device__ __forceinline__ void copy(const void *src, size_t i, void *dst, size_t j) {
-        const float4 *s = reinterpret_cast<const float4 *>(static_cast<const float *>(src) + i);
-        float4 *d = reinterpret_cast<float4 *>(static_cast<float *>(dst) + j);
-        float4 a = s[0], b = s[1];
-        d[0] = a;
-        d[1] = b;
+};
+
+// Storage column of key channel c in a channel-permuted [*][128] plane.
+__device__ __forceinline__ int cperm(int c) { return (c & ~31) | kperm(c & 31); }
+
+// Column swizzle of the Khat^T planes: row c keeps its 4-token groups
+// contiguous (8-byte MFMA operand reads) but XORs the group index with
+// (c / 8) % 4, spreading the transposed stores of 16 lanes (rows 8 apart)
+// over four bank groups.
+__device__ __forceinline__ int kht_col(int c, int j) { return j ^ (((c >> 3) & 3) << 2); }
+
+// Range-checked buffer view of one head's rows [r0, r_end) of a [T][H][128]
+// (or [T][H]) tensor: loads past the view (or before it, through a negative
+// row offset that wraps) return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_view(const void *base, size_t first_elem,
+                                                             int elt_bytes, int n_rows, size_t row_elems,
+                                                             int row_len) {
+    const char *b = static_cast<const char *>(base) + first_elem * elt_bytes;
+    const int bytes = n_rows > 0 ? static_cast<int>(((n_rows - 1) * row_elems + row_len) * elt_bytes) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(b), static_cast<short>(0), bytes, 0x00020000);
+}
+
+template <typename IO> struct BufLoad8;
+template <> struct BufLoad8<uint16_t> {
+    using Raw = typename Vec8<uint16_t>::Raw;
+    static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+        u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+        return Raw{make_uint4(v[0], v[1], v[2], v[3])};
+    }
+};
+template <> struct BufLoad8<float> {
+    using Raw = typename Vec8<float>::Raw;
+    static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+        u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+        u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off + 16, 0, 0);
+        return Raw{make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3])),
+                   make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3]))};
     }
 };
 
 template <typename IO, typename OUT>
-__global__ __launch_bounds__(THREADS) void chunked_kernel(LayerParams p) {
+__global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_kernel(LayerParams p) {
     using IV = Vec8<IO>;
+    using IB = BufLoad8<IO>;
     using OV = Vec8<OUT>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[RawLds<IO>::BYTES];
+    IO *const RAWC = reinterpret_cast<IO *>(smem + RawLds<IO>::CUR);
+    IO *const RAWH = reinterpret_cast<IO *>(smem + RawLds<IO>::HIST);
     uint16_t *const KLh = reinterpret_cast<uint16_t *>(smem + OFF_KL);
     uint16_t *const QLh = reinterpret_cast<uint16_t *>(smem + OFF_QL);
     uint16_t *const KRDh = reinterpret_cast<uint16_t *>(smem + OFF_KRD);
-    uint16_t *const KR10h = reinterpret_cast<uint16_t *>(smem + OFF_KR10);
-    uint16_t *const KBNh = reinterpret_cast<uint16_t *>(smem + OFF_KBN);
-    uint16_t *const QBh = reinterpret_cast<uint16_t *>(smem + OFF_QB);
     uint16_t *const KHTh = reinterpret_cast<uint16_t *>(smem + OFF_KHT);
     uint16_t *const PMh = reinterpret_cast<uint16_t *>(smem + OFF_PM);
     uint16_t *const TMh = reinterpret_cast<uint16_t *>(smem + OFF_TM);
-    float *const VB = reinterpret_cast<float *>(smem + OFF_V);
     float *const OB = reinterpret_cast<float *>(smem + OFF_O);
+    float *const VB = reinterpret_cast<float *>(smem + OFF_V);
     float *const LA = reinterpret_cast<float *>(smem + OFF_LA);
     float *const AF = reinterpret_cast<float *>(smem + OFF_AF);
-    float *const TS = reinterpret_cast<float *>(smem + OFF_TS);
     float *const BETA = reinterpret_cast<float *>(smem + OFF_BETA);
-    float *const ER1 = reinterpret_cast<float *>(smem + OFF_ER1);
-    float *const ET1 = reinterpret_cast<float *>(smem + OFF_ET1);
     float *const EGC = reinterpret_cast<float *>(smem + OFF_EGC);
     float *const CW = reinterpret_cast<float *>(smem + OFF_CW);
     float *const RW = reinterpret_cast<float *>(smem + OFF_RW);
@@ -221,73 +284,122 @@ __global__ __launch_bounds__(THREADS) void chunked_kernel(LayerParams p) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int ln = lane & 15;   // MFMA row / column index
-    const int lh = lane >> 4;   // MFMA K group
-    const int et = tid >> 4;    // element-wise token (0..31)
+    const int ln = lane & 15;        // MFMA row / column index
+    const int lh = lane >> 4;        // MFMA K group
+    const int et = tid >> 4;         // element-wise token (0..15)
     const int ec0 = (tid & 15) * 8;  // element-wise first channel
-    const int col = wave * 16 + ln;  // this lane's value column of S
+    const int col0 = wave * 32 + ln; // value column of N-tile 0 (tile 1: +16)
 
-    // ---- per-head constants -------------------------------------------------------
+    // ---- per-head constants -----------------------------------------------------------
     if (p.prologue) {
         for (int i = tid; i < 3 * D; i += THREADS) {
             const int s = i / D, c = i % D;
             const float4 w = *reinterpret_cast<const float4 *>(p.conv_w + ((s * HD) + hD + c) * 4);
-            *reinterpret_cast<float4 *>(CW + i * 4) = w;
+            CW[(s * 4 + 0) * D + c] = w.x;
+            CW[(s * 4 + 1) * D + c] = w.y;
+            CW[(s * 4 + 2) * D + c] = w.z;
+            CW[(s * 4 + 3) * D + c] = w.w;
         }
     }
     if (tid < D) RW[tid] = p.rms_w ? p.rms_w[tid] : 1.0f;
 
-    // ---- state slice in accumulator layout ------------------------------------------
+    // ---- state slice in accumulator layout: S[t][nt][i] = S(16t + 4lh + i, col0 + 16nt) ----
     const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D;
-    f32x4_t S[8];
+    f32x4_t S[8][2];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[t][i] = p.state_in ? p.state_in[sbase + static_cast<size_t>(16 * t + 4 * lh + i) * D + col] : 0.0f;
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[t][nt][i] = p.state_in ? p.state_in[sbase + static_cast<size_t>(16 * t + 4 * lh + i) * D + col0 + 16 * nt] : 0.0f;
 
     const int nchunks = (L + C - 1) / C;
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int pos = ch * C + et;          // position of this thread's token in the sequence
-        const bool valid = pos < L;
-        const size_t grow = static_cast<size_t>(t0 + pos);
+    const void *srcs[3] = {p.q, p.k, p.v};
 
-        // ---- 1. prologue: conv4 + SiLU (+ L2 for q, k), gates ---------------------------
+    // Current-row loads of a chunk (q, k, v, log alpha, beta): issued one chunk ahead,
+    // during the previous chunk's state products, so that their latency is hidden.
+    typename IV::Raw cur[3];
+    typename Vec8<float>::Raw lar;
+    float bet = 0.0f;
+    typename IV::Raw graw;
+    auto load_current = [&](int c) {
+        const int r0 = c * C, nrow = min(L, r0 + C) - r0;
+        const uint32_t o_io = static_cast<uint32_t>(et * static_cast<int>(HD) + ec0) * sizeof(IO);
+#pragma unroll
+        for (int s = 0; s < 3; ++s)
+            cur[s] = IB::load(rows_view(srcs[s], (t0 + r0) * HD + hD, sizeof(IO), nrow, HD, D), o_io);
+        lar = BufLoad8<float>::load(rows_view(p.log_alpha, (t0 + r0) * HD + hD, 4, nrow, HD, D),
+                                    static_cast<uint32_t>(et * static_cast<int>(HD) + ec0) * 4u);
+        bet = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rows_view(p.beta, (t0 + r0) * H + h, 4, nrow, H, 1), static_cast<uint32_t>(et * H) * 4u, 0, 0));
+    };
+    auto load_gate = [&](int c) {
+        const int r0 = c * C, nrow = min(L, r0 + C) - r0;
+        if (p.epilogue)
+            graw = IB::load(rows_view(p.g, (t0 + r0) * HD + hD, sizeof(IO), nrow, HD, D),
+                            static_cast<uint32_t>(et * static_cast<int>(HD) + ec0) * sizeof(IO));
+    };
+    if (nchunks > 0) {
+        load_current(0);
+        load_gate(0);
+    }
+    if (p.prologue && tid < 3 * CONV_HIST * 16) {
+        // history of the first chunk: the given conv cache (oldest first) or zeros
+        const int s = tid / (CONV_HIST * 16), j = (tid / 16) % CONV_HIST, c0 = (tid & 15) * 8;
+        typename IV::Raw r{};
+        if (p.conv_in) r = IV::raw(p.conv_in, ((static_cast<size_t>(n) * 3 + s) * CONV_HIST + j) * HD + hD + c0);
+        *reinterpret_cast<typename IV::Raw *>(RAWH + ((1 * 3 + s) * CONV_HIST + j) * D + c0) = r;
+    }
+
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int r0 = ch * C;                 // first position of the chunk
+        const int rend = min(L, r0 + C);       // end of the chunk's valid rows
+        const int pos = r0 + et;               // this thread's token position
+        const bool valid = pos < L;
+
+        // ---- 1. stage this chunk's raw rows (prefetched during the previous chunk) -------------
+        const int hb = ch & 1;  // history buffer written by this chunk (read by the next)
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            *reinterpret_cast<typename IV::Raw *>(RAWC + (s * C + et) * D + ec0) = cur[s];
+            if (et >= C - CONV_HIST)
+                *reinterpret_cast<typename IV::Raw *>(RAWH + ((hb * 3 + s) * CONV_HIST + et - (C - CONV_HIST)) * D + ec0) = cur[s];
+        }
+        {
+            float la[8];
+            Vec8<float>::unpack(lar, la);
+            Vec8<float>::store(LA, et * D + ec0, la);
+            if ((tid & 15) == 0) BETA[et] = bet;
+        }
+        __syncthreads();
+
+        // ---- 2. conv4 + SiLU (+ L2 for q, k) from the staged rows; cumulative log-decay -------
         float xq[8], xk[8], xv[8];
         {
             float *outs[3] = {xq, xk, xv};
-            const void *srcs[3] = {p.q, p.k, p.v};
 #pragma unroll
             for (int s = 0; s < 3; ++s) {
                 float *a = outs[s];
-                float x0[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x0[e] = 0.0f;
-                if (valid) IV::load(srcs[s], grow * HD + hD + ec0, x0);
+                IV::unpack(*reinterpret_cast<const typename IV::Raw *>(RAWC + (s * C + et) * D + ec0), a);
                 if (p.prologue) {
-                    float acc[8];
+                    float acc[8], w[8];
+                    Vec8<float>::load(CW, (s * 4) * D + ec0, w);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] = CW[(s * D + ec0 + e) * 4] * x0[e];
+                    for (int e = 0; e < 8; ++e) acc[e] = w[e] * a[e];
 #pragma unroll
                     for (int j = 1; j <= 3; ++j) {
+                        const int r = et - j;  // row in this chunk, or (r + 3) in the history
+                        const IO *src = r >= 0 ? RAWC + (s * C + r) * D
+                                               : RAWH + (((hb ^ 1) * 3 + s) * CONV_HIST + r + CONV_HIST) * D;
                         float xj[8];
+                        IV::unpack(*reinterpret_cast<const typename IV::Raw *>(src + ec0), xj);
+                        Vec8<float>::load(CW, (s * 4 + j) * D + ec0, w);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) xj[e] = 0.0f;
-                        const int pj = pos - j;
-                        if (valid) {
-                            if (pj >= 0)
-                                IV::load(srcs[s], (grow - j) * HD + hD + ec0, xj);
-                            else if (p.conv_in)
-                                IV::load(p.conv_in, ((static_cast<size_t>(n) * 3 + s) * CONV_HIST + (CONV_HIST + pj)) * HD + hD + ec0, xj);
-                        }
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[e] = fmaf(CW[(s * D + ec0 + e) * 4 + j], xj[e], acc[e]);
+                        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[e], xj[e], acc[e]);
                     }
 #pragma unroll
                     for (int e = 0; e < 8; ++e) a[e] = siluf_(acc[e]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) a[e] = x0[e];
                 }
             }
             if (p.prologue) {
@@ -305,51 +417,29 @@ __global__ __launch_bounds__(THREADS) void chunked_kernel(LayerParams p) {
                     xq[e] *= iq;
                     xk[e] *= ik;
                 }
-            }
-            if (!valid) {
+                if (!valid) {  // padding tokens past the end see real history rows: clear them
 #pragma unroll
-                for (int e = 0; e < 8; ++e) xq[e] = xk[e] = xv[e] = 0.0f;
+                    for (int e = 0; e < 8; ++e) xq[e] = xk[e] = xv[e] = 0.0f;
+                }
             }
-            float la[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) la[e] = 0.0f;
-            if (valid) Vec8<float>::load(p.log_alpha, grow * HD + hD + ec0, la);
-            Vec8<float>::store(LA, et * D + ec0, la);
-            if ((tid & 15) == 0) BETA[et] = valid ? p.beta[grow * H + h] : 0.0f;
         }
-        __syncthreads();
-
-        // ---- 2. local cumulative log-decay inside each 16-token sub-tile --------------------
         if (tid < D) {
             const int c = tid;
-            float g[C];
+            float g = 0.0f;
 #pragma unroll
-            for (int r = 0; r < C; ++r) g[r] = LA[r * D + c];
-#pragma unroll
-            for (int r = 1; r < SUBT; ++r) {
-                g[r] += g[r - 1];
-                g[SUBT + r] += g[SUBT + r - 1];
+            for (int r = 0; r < C; ++r) {
+                g += LA[r * D + c];
+                LA[r * D + c] = g;
             }
-#pragma unroll
-            for (int r = 0; r < C; ++r) LA[r * D + c] = g[r];
-            const float tot0 = g[SUBT - 1], tot1 = g[C - 1];
-            ER1[c] = __expf(tot0);
-            ET1[c] = __expf(tot1);
-            EGC[c] = __expf(tot0 + tot1);
+            EGC[c] = __expf(g);
         }
         __syncthreads();
 
-        // ---- 3. staged operands (hi/lo bf16) ------------------------------------------
+        // ---- 3. staged operands (bf16 hi/lo) ------------------------------------------------
         {
-            const int sig = et >> 4;  // sub-tile of this token
-            float gl[8], er[8], egcr[8];
+            float gl[8];
             Vec8<float>::load(LA, et * D + ec0, gl);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                er[e] = sig ? ER1[ec0 + e] : 1.0f;
-                egcr[e] = sig ? ET1[ec0 + e] : EGC[ec0 + e];
-            }
-            float kl[8], ql[8], krd[8], tmp[8];
+            float kl[8], ql[8], krd[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float E = __expf(gl[e]);
@@ -358,231 +448,197 @@ __global__ __launch_bounds__(THREADS) void chunked_kernel(LayerParams p) {
                 ql[e] = xq[e] * E;
                 krd[e] = xk[e] * rE;
             }
-            uint4 hi, lo;
-            const int ro = et * OPK + ec0;
-            split8(kl, hi, lo);
-            *reinterpret_cast<uint4 *>(KLh + ro) = hi;
-            *reinterpret_cast<uint4 *>(KLh + PL_C_D + ro) = lo;
-            split8(ql, hi, lo);
-            *reinterpret_cast<uint4 *>(QLh + ro) = hi;
-            *reinterpret_cast<uint4 *>(QLh + PL_C_D + ro) = lo;
-            split8(krd, hi, lo);
-            *reinterpret_cast<uint4 *>(KRDh + ro) = hi;
-            *reinterpret_cast<uint4 *>(KRDh + PL_C_D + ro) = lo;
-            if (sig == 0) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) tmp[e] = krd[e] * ER1[ec0 + e];
-                split8(tmp, hi, lo);
-                *reinterpret_cast<uint4 *>(KR10h + ro) = hi;
-                *reinterpret_cast<uint4 *>(KR10h + PL_S_D + ro) = lo;
-            }
-            // K-permuted channel position of channels ec0..ec0+3 and ec0+4..ec0+7
-            const int cb = ec0 & ~31, a4 = (ec0 >> 3) & 3;
-            const int pc0 = cb + 16 * (a4 & 1) + 4 * (a4 >> 1);
-            const int pc1 = pc0 + 8;
+            // channel-permuted positions of channels ec0..ec0+3 and ec0+4..ec0+7
+            const int pc0 = cperm(ec0), pc1 = cperm(ec0 + 4);
             const int rp = et * OPK;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tmp[e] = -kl[e] * er[e];
-            split8(tmp, hi, lo);
-            *reinterpret_cast<uint2 *>(KBNh + rp + pc0) = make_uint2(hi.x, hi.y);
-            *reinterpret_cast<uint2 *>(KBNh + rp + pc1) = make_uint2(hi.z, hi.w);
-            *reinterpret_cast<uint2 *>(KBNh + PL_C_D + rp + pc0) = make_uint2(lo.x, lo.y);
-            *reinterpret_cast<uint2 *>(KBNh + PL_C_D + rp + pc1) = make_uint2(lo.z, lo.w);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tmp[e] = ql[e] * er[e];
-            split8(tmp, hi, lo);
-            *reinterpret_cast<uint2 *>(QBh + rp + pc0) = make_uint2(hi.x, hi.y);
-            *reinterpret_cast<uint2 *>(QBh + rp + pc1) = make_uint2(hi.z, hi.w);
-            *reinterpret_cast<uint2 *>(QBh + PL_C_D + rp + pc0) = make_uint2(lo.x, lo.y);
-            *reinterpret_cast<uint2 *>(QBh + PL_C_D + rp + pc1) = make_uint2(lo.z, lo.w);
-            // Khat^T: row = channel, column = K-permuted token
-            const int pt = kperm(et);
+            uint4 hi, lo;
+            split8(kl, hi, lo);
+            *reinterpret_cast<uint2 *>(KLh + rp + pc0) = make_uint2(hi.x, hi.y);
+            *reinterpret_cast<uint2 *>(KLh + rp + pc1) = make_uint2(hi.z, hi.w);
+            *reinterpret_cast<uint2 *>(KLh + PL_CD + rp + pc0) = make_uint2(lo.x, lo.y);
+            *reinterpret_cast<uint2 *>(KLh + PL_CD + rp + pc1) = make_uint2(lo.z, lo.w);
+            split8(ql, hi, lo);
+            *reinterpret_cast<uint2 *>(QLh + rp + pc0) = make_uint2(hi.x, hi.y);
+            *reinterpret_cast<uint2 *>(QLh + rp + pc1) = make_uint2(hi.z, hi.w);
+            *reinterpret_cast<uint2 *>(QLh + PL_CD + rp + pc0) = make_uint2(lo.x, lo.y);
+            *reinterpret_cast<uint2 *>(QLh + PL_CD + rp + pc1) = make_uint2(lo.z, lo.w);
+            split8(krd, hi, lo);
+            *reinterpret_cast<uint2 *>(KRDh + rp + pc0) = make_uint2(hi.x, hi.y);
+            *reinterpret_cast<uint2 *>(KRDh + rp + pc1) = make_uint2(hi.z, hi.w);
+            *reinterpret_cast<uint2 *>(KRDh + PL_CD + rp + pc0) = make_uint2(lo.x, lo.y);
+            *reinterpret_cast<uint2 *>(KRDh + PL_CD + rp + pc1) = make_uint2(lo.z, lo.w);
+            // Khat^T[c][t] = k^_t[c] e^{G_C[c] - G_t[c]}
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                const int c = ec0 + e;
                 uint16_t sh, sl;
-                split1(krd[e] * egcr[e], sh, sl);
-                KHTh[(ec0 + e) * OPT + pt] = sh;
-                KHTh[PL_D_C + (ec0 + e) * OPT + pt] = sl;
+                split1(krd[e] * EGC[c], sh, sl);
+                KHTh[c * OPT + kht_col(c, et)] = sh;
+                KHTh[PL_DC + c * OPT + kht_col(c, et)] = sl;
             }
+            Vec8<float>::store(VB, et * FPK + ec0, xv);
         }
         __syncthreads();
 
-        // ---- 4. intra-chunk Gram blocks on MFMA ----------------------------------------
-        // waves 0-2: A blocks (0,0), (1,0), (1,1); waves 3-5: P blocks; wave 6 clears P's
-        // upper-right block.
-        if (wave < 6) {
-            const bool isP = wave >= 3;
-            const int pr = wave % 3;
-            const int sg = pr == 0 ? 0 : 1;          // row sub-tile
-            const int tg = pr == 2 ? 1 : 0;          // column sub-tile
-            const uint16_t *Lh = isP ? QLh : KLh;
-            const uint16_t *Rh = pr == 1 ? KR10h : KRDh;
-            const int rplane = pr == 1 ? PL_S_D : PL_C_D;
-            const int rrow = pr == 1 ? 0 : 16 * tg;
+        // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
+        if (wave < 2) {
+            const uint16_t *Lh = wave == 0 ? KLh : QLh;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < D / 32; ++s) {
-                const int ka = (16 * sg + ln) * OPK + 32 * s + 8 * lh;
-                const int kb = (rrow + ln) * OPK + 32 * s + 8 * lh;
+                const int ka = ln * OPK + 32 * s + 8 * lh;
                 const uint4 ah = *reinterpret_cast<const uint4 *>(Lh + ka);
-                const uint4 al = *reinterpret_cast<const uint4 *>(Lh + PL_C_D + ka);
-                const uint4 bh = *reinterpret_cast<const uint4 *>(Rh + kb);
-                const uint4 bl = *reinterpret_cast<const uint4 *>(Rh + rplane + kb);
+                const uint4 al = *reinterpret_cast<const uint4 *>(Lh + PL_CD + ka);
+                const uint4 bh = *reinterpret_cast<const uint4 *>(KRDh + ka);
+                const uint4 bl = *reinterpret_cast<const uint4 *>(KRDh + PL_CD + ka);
                 acc = mma3(ah, al, bh, bl, acc);
             }
-            const bool diag = sg == tg;
+            const int j = ln;
+            if (wave == 0) {
+                // T = (I + A)^{-1} Diag(beta).  With B = -A (strictly lower, so B^16 = 0),
+                // (I + A)^{-1} = sum_{k<16} B^k = (I + B)(I + B^2)(I + B^4)(I + B^8):
+                // four levels of 16x16 products on the matrix cores.  Every matrix M is
+                // kept in two register forms: "b" = B-operand / accumulator layout (lane
+                // (n, g) holds M[4g+i][n]) and "a" = A-operand layout (lane (m, g) holds
+                // M[m][4g+i]); the product XY takes (a of X, b of Y) and gives b of XY,
+                // while (b of Y, a of X) gives b of (XY)^T = a of XY.
+                float bb[4], ba[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * sg + 4 * lh + i;  // output token (row)
-                const int j = 16 * tg + ln;          // input token (column)
-                if (!isP) {
-                    AF[r * 33 + j] = (diag && j >= r) ? 0.0f : acc[i] * BETA[r];
-                } else {
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * lh + i;
+                    bb[i] = j < r ? -acc[i] * BETA[r] : 0.0f;
+                    AF[r * 17 + j] = bb[i];
+                }
+                // one transpose through LDS for the a form of B
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ba[i] = AF[ln * 17 + 4 * lh + i];
+                float sb[4], sa[4];  // S1 = I + B
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sb[i] = bb[i] + ((4 * lh + i) == ln ? 1.0f : 0.0f);
+                    sa[i] = ba[i] + ((4 * lh + i) == ln ? 1.0f : 0.0f);
+                }
+                float b2b[4], b2a[4], t[4];
+                mm16(ba, bb, b2b);                      // B^2
+                mm16(bb, ba, b2a);
+                float b4b[4], b4a[4];
+                mm16(sa, b2b, t);                       // S2 = S1 + S1 B^2
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sb[i] += t[i];
+                mm16(b2b, sa, t);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sa[i] += t[i];
+                mm16(b2a, b2b, b4b);                    // B^4
+                mm16(b2b, b2a, b4a);
+                mm16(sa, b4b, t);                       // S4 = S2 + S2 B^4
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sb[i] += t[i];
+                mm16(b4b, sa, t);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sa[i] += t[i];
+                float b8b[4];
+                mm16(b4a, b4b, b8b);                    // B^8
+                mm16(b8b, sa, t);                       // a form of S8 = S4 + S4 B^8
+                // T[m][k] = S8[m][k] beta_k: lane (m, g) stores row m, columns 4g .. 4g+3
+                float tv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tv[i] = (sa[i] + t[i]) * BETA[4 * lh + i];
+                uint2 th, tl;
+                split4(tv, th, tl);
+                *reinterpret_cast<uint2 *>(TMh + ln * OPT + 4 * lh) = th;
+                *reinterpret_cast<uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh) = tl;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 4 * lh + i;
                     uint16_t sh, sl;
-                    split1((diag && j > r) ? 0.0f : acc[i], sh, sl);
-                    PMh[r * OPT + kperm(j)] = sh;
-                    PMh[PL_C_C + r * OPT + kperm(j)] = sl;
+                    split1(j <= r ? acc[i] : 0.0f, sh, sl);
+                    PMh[r * OPT + j] = sh;
+                    PMh[PL_CC + r * OPT + j] = sl;
                 }
             }
-        } else if (wave == 6) {
-            // P[r][j] = 0 for r < 16 <= j
-            for (int e = lane; e < 16 * 16; e += 64) {
-                const int r = e >> 4, j = 16 + (e & 15);
-                PMh[r * OPT + kperm(j)] = 0;
-                PMh[PL_C_C + r * OPT + kperm(j)] = 0;
+        }
+        // X = V - Kbar S0 and O1 = Qbar S0.  S0 is the B operand: K step s holds rows
+        // 32s + pi(slot), split into bf16 hi/lo right before use.
+        f32x4_t X[2], O1[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            X[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            O1[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int ka = ln * OPK + 32 * s + 8 * lh;
+            const uint4 kh = *reinterpret_cast<const uint4 *>(KLh + ka);
+            const uint4 kl_ = *reinterpret_cast<const uint4 *>(KLh + PL_CD + ka);
+            const uint4 qh = *reinterpret_cast<const uint4 *>(QLh + ka);
+            const uint4 ql_ = *reinterpret_cast<const uint4 *>(QLh + PL_CD + ka);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const float v8[8] = {S[2 * s][nt][0], S[2 * s][nt][1], S[2 * s][nt][2], S[2 * s][nt][3],
+                                     S[2 * s + 1][nt][0], S[2 * s + 1][nt][1], S[2 * s + 1][nt][2], S[2 * s + 1][nt][3]};
+                uint4 sh, sl;
+                split8(v8, sh, sl);
+                X[nt] = mma3(kh, kl_, sh, sl, X[nt]);
+                O1[nt] = mma3(qh, ql_, sh, sl, O1[nt]);
             }
         }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X[nt][i] = VB[(4 * lh + i) * FPK + col0 + 16 * nt] - X[nt][i];
         __syncthreads();
 
-        // ---- 5. V tile (fp32) and T = (I + A)^{-1} Diag(beta) -----------------------------
-        Vec8<float>::store(VB, et * FPK + ec0, xv);
-        if (tid < 32) {
-            // column c of the inverse of the unit-lower 16x16 block I + A_bb
-            const int b = tid >> 4, c = tid & 15;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == c) ? 1.0f : 0.0f;
-#pragma unroll
-                for (int j = 0; j < r; ++j) acc = fmaf(-AF[(16 * b + r) * 33 + 16 * b + j], x[j], acc);
-                x[r] = acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) TS[(b * 16 + r) * 17 + c] = x[r];
-        }
-        __syncthreads();
-        if (tid < 256) {
-            // Z = A_10 D0^{-1}
-            const int r = tid >> 4, c = tid & 15;
-            float acc = 0.f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc = fmaf(AF[(16 + r) * 33 + j], TS[j * 17 + c], acc);
-            TS[(32 + r) * 17 + c] = acc;
-        }
-        __syncthreads();
-        if (tid < 256) {
-            // T_10 = -D1^{-1} Z Diag(beta_0..15)
-            const int r = tid >> 4, c = tid & 15;
-            float acc = 0.f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) acc = fmaf(TS[(16 + r) * 17 + j], TS[(32 + j) * 17 + c], acc);
-            uint16_t sh, sl;
-            split1(-acc * BETA[c], sh, sl);
-            TMh[(16 + r) * OPT + kperm(c)] = sh;
-            TMh[PL_C_C + (16 + r) * OPT + kperm(c)] = sl;
-        } else {
-            for (int e = tid - 256; e < 3 * 256; e += 256) {
-                const int blk = e >> 8, r = (e >> 4) & 15, c = e & 15;
-                float v;
-                int rr, cc;
-                if (blk == 0) { v = TS[r * 17 + c] * BETA[c]; rr = r; cc = c; }
-                else if (blk == 1) { v = TS[(16 + r) * 17 + c] * BETA[16 + c]; rr = 16 + r; cc = 16 + c; }
-                else { v = 0.0f; rr = r; cc = 16 + c; }
-                uint16_t sh, sl;
-                split1(v, sh, sl);
-                TMh[rr * OPT + kperm(cc)] = sh;
-                TMh[PL_C_C + rr * OPT + kperm(cc)] = sl;
-            }
-        }
-        __syncthreads();
-
-        // ---- 6. state contractions (this wave's 16 value columns) -------------------------
+        // ---- 5. U = T X, O = scale (Qbar S + P U), S <- Diag(Gamma_C) S + Khat^T U -------------
+        if (ch + 1 < nchunks) load_current(ch + 1);
         {
-            // S as B operand: K step s holds rows 32s + pi(slot)
-            uint4 Sh[4], Sl[4];
+            uint2 Th, Tl, Ph, Pl;
+            Th = *reinterpret_cast<const uint2 *>(TMh + ln * OPT + 4 * lh);
+            Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh);
+            Ph = *reinterpret_cast<const uint2 *>(PMh + ln * OPT + 4 * lh);
+            Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + ln * OPT + 4 * lh);
+            uint2 Uh[2], Ul[2];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float v8[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
-                                     S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
-                split8(v8, Sh[s], Sl[s]);
+            for (int nt = 0; nt < 2; ++nt) {
+                uint2 xh, xl;
+                const float x4[4] = {X[nt][0], X[nt][1], X[nt][2], X[nt][3]};
+                split4(x4, xh, xl);
+                const f32x4_t U = mma16_3(Th, Tl, xh, xl, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                const float u4[4] = {U[0], U[1], U[2], U[3]};
+                split4(u4, Uh[nt], Ul[nt]);
             }
-            // X = V - Kbar S
-            f32x4_t X[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
+            for (int nt = 0; nt < 2; ++nt) {
+                // P U goes to its own accumulator: a K = 16 MFMA accumulating onto the result of
+                // a K = 32 MFMA read stale accumulator rows on gfx950 (observed, not documented),
+                // so the two chains never share an accumulator and are summed on the VALU.
+                const f32x4_t O2 = mma16_3(Ph, Pl, Uh[nt], Ul[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                for (int i = 0; i < 4; ++i) X[mt][i] = VB[(16 * mt + 4 * lh + i) * FPK + col];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int ka = (16 * mt + ln) * OPK + 32 * s + 8 * lh;
-                    const uint4 ah = *reinterpret_cast<const uint4 *>(KBNh + ka);
-                    const uint4 al = *reinterpret_cast<const uint4 *>(KBNh + PL_C_D + ka);
-                    X[mt] = mma3(ah, al, Sh[s], Sl[s], X[mt]);
-                }
+                for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col0 + 16 * nt] = (O1[nt][i] + O2[i]) * p.scale;
             }
-            // U = T X
-            uint4 Xh, Xl;
-            {
-                const float v8[8] = {X[0][0], X[0][1], X[0][2], X[0][3], X[1][0], X[1][1], X[1][2], X[1][3]};
-                split8(v8, Xh, Xl);
-            }
-            f32x4_t U[2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int ka = (16 * mt + ln) * OPT + 8 * lh;
-                const uint4 ah = *reinterpret_cast<const uint4 *>(TMh + ka);
-                const uint4 al = *reinterpret_cast<const uint4 *>(TMh + PL_C_C + ka);
-                U[mt] = mma3(ah, al, Xh, Xl, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            }
-            uint4 Uh, Ul;
-            {
-                const float v8[8] = {U[0][0], U[0][1], U[0][2], U[0][3], U[1][0], U[1][1], U[1][2], U[1][3]};
-                split8(v8, Uh, Ul);
-            }
-            // O = scale (Qbar S + P U)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int ka = (16 * mt + ln) * OPK + 32 * s + 8 * lh;
-                    const uint4 ah = *reinterpret_cast<const uint4 *>(QBh + ka);
-                    const uint4 al = *reinterpret_cast<const uint4 *>(QBh + PL_C_D + ka);
-                    O = mma3(ah, al, Sh[s], Sl[s], O);
-                }
-                {
-                    const int ka = (16 * mt + ln) * OPT + 8 * lh;
-                    const uint4 ah = *reinterpret_cast<const uint4 *>(PMh + ka);
-                    const uint4 al = *reinterpret_cast<const uint4 *>(PMh + PL_C_C + ka);
-                    O = mma3(ah, al, Uh, Ul, O);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) OB[(16 * mt + 4 * lh + i) * FPK + col] = O[i] * p.scale;
-            }
-            // S <- Diag(Gamma_C) S + Khat^T U
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
+                const int c = 16 * t + ln;
+                const int ka = c * OPT + kht_col(c, 4 * lh);
+                const uint2 ah = *reinterpret_cast<const uint2 *>(KHTh + ka);
+                const uint2 al = *reinterpret_cast<const uint2 *>(KHTh + PL_DC + ka);
+                float g4[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[t][i] *= EGC[16 * t + 4 * lh + i];
-                const int ka = (16 * t + ln) * OPT + 8 * lh;
-                const uint4 ah = *reinterpret_cast<const uint4 *>(KHTh + ka);
-                const uint4 al = *reinterpret_cast<const uint4 *>(KHTh + PL_D_C + ka);
-                S[t] = mma3(ah, al, Uh, Ul, S[t]);
+                for (int i = 0; i < 4; ++i) g4[i] = EGC[16 * t + 4 * lh + i];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[t][nt][i] *= g4[i];
+                    S[t][nt] = mma16_3(ah, al, Uh[nt], Ul[nt], S[t][nt]);
+                }
             }
         }
         __syncthreads();
 
-        // ---- 7. epilogue: sigma(g) * RMSNorm(o~) * w -------------------------------------
+        // ---- 6. epilogue: sigma(g) * RMSNorm(o~) * w ------------------------------------------
         {
             float o[8];
             Vec8<float>::load(OB, et * FPK + ec0, o);
@@ -592,25 +648,26 @@ __global__ __launch_bounds__(THREADS) void chunked_kernel(LayerParams p) {
                 for (int e = 0; e < 8; ++e) ss = fmaf(o[e], o[e], ss);
                 ss = group_sum<16>(ss);
                 const float inv = rsqrtf(ss * (1.0f / D) + p.rms_eps);
-                if (valid) {
-                    float g[8];
-                    IV::load(p.g, grow * HD + hD + ec0, g);
+                float g[8];
+                IV::unpack(graw, g);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) o[e] = sigmoidf_(g[e]) * (o[e] * inv) * RW[ec0 + e];
-                }
+                for (int e = 0; e < 8; ++e) o[e] = sigmoidf_(g[e]) * (o[e] * inv) * RW[ec0 + e];
             }
-            if (valid) OV::store(p.o, grow * HD + hD + ec0, o);
+            if (valid) OV::store(p.o, static_cast<size_t>(t0 + pos) * HD + hD + ec0, o);
         }
-        // the next chunk's first barrier orders these LDS reads before any rewrite
+        if (ch + 1 < nchunks) load_gate(ch + 1);
+        // the next chunk's first two barriers order these LDS reads before any rewrite
     }
 
-    // ---- final state and conv cache -----------------------------------------------------
+    // ---- final state and conv cache ------------------------------------------------------
     if (p.state_out) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                p.state_out[sbase + static_cast<size_t>(16 * t + 4 * lh + i) * D + col] = S[t][i];
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p.state_out[sbase + static_cast<size_t>(16 * t + 4 * lh + i) * D + col0 + 16 * nt] = S[t][nt][i];
     }
     if (p.prologue && p.conv_out) {
         // the last three pre-conv inputs of each stream, oldest first; rows before the

@@ -69,7 +69,9 @@ template <> struct IoTraits<uint16_t> {  // bf16 stored as raw bits
     }
 };
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
-__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + __expf(-x)); }
+// sigma(x) and x * sigma(x) with the hardware reciprocal (about 1 ulp) in place of
+// an IEEE division; exp(-x) overflowing to inf gives the correct limit 0.
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 }  // namespace kda

@@ -136,13 +136,22 @@ __device__ __forceinline__ f32x4_t mma16_3(uint2 ahi, uint2 alo, uint2 bhi, uint
     return mma16(ahi, bhi, c);
 }
 
-// d = x y for 16x16 fp32 matrices held as (a form of x, b form of y), through
-// bf16 hi/lo operand splits on a fresh accumulator.
-__device__ __forceinline__ void mm16(const float *xa, const float *yb, float *d) {
-    uint2 ah, al, bh, bl;
-    split4(xa, ah, al);
-    split4(yb, bh, bl);
-    const f32x4_t r = mma16_3(ah, al, bh, bl, f32x4_t{0.f, 0.f, 0.f, 0.f});
+// A 16x16 fp32 matrix fragment (4 values per lane) split into bf16 hi/lo.
+struct Split4 {
+    uint2 h, l;
+    __device__ __forceinline__ explicit Split4(const float *x) { split4(x, h, l); }
+    __device__ __forceinline__ explicit Split4(const f32x4_t &x) {
+        const float v[4] = {x[0], x[1], x[2], x[3]};
+        split4(v, h, l);
+    }
+};
+
+// x y for 16x16 matrices held as (a form of x, b form of y), on a fresh accumulator.
+__device__ __forceinline__ f32x4_t mm16s(const Split4 &xa, const Split4 &yb) {
+    return mma16_3(xa.h, xa.l, yb.h, yb.l, f32x4_t{0.f, 0.f, 0.f, 0.f});
+}
+__device__ __forceinline__ void mm16s(const Split4 &xa, const Split4 &yb, float *d) {
+    const f32x4_t r = mm16s(xa, yb);
     d[0] = r[0]; d[1] = r[1]; d[2] = r[2]; d[3] = r[3];
 }
 
@@ -183,13 +192,15 @@ template <> struct Vec8<uint16_t> {
         }
     }
     static __device__ __forceinline__ void load(const void *p, size_t i, float *x) { unpack(raw(p, i), x); }
-    static __device__ __forceinline__ void store(void *p, size_t i, const float *x) {
+    static __device__ __forceinline__ uint4 pack(const float *x) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            w[e] = static_cast<uint32_t>(f32_to_bf16(x[2 * e])) |
-                   (static_cast<uint32_t>(f32_to_bf16(x[2 * e + 1])) << 16);
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p) + i) = make_uint4(w[0], w[1], w[2], w[3]);
+            w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x[2 * e], x[2 * e + 1]}, bf16x2_t));
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    static __device__ __forceinline__ void store(void *p, size_t i, const float *x) {
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p) + i) = pack(x);
     }
 };
 template <> struct Vec8<float> {
@@ -219,15 +230,14 @@ __device__ __forceinline__ int cperm(int c) { return (c & ~31) | kperm(c & 31); 
 // over four bank groups.
 __device__ __forceinline__ int kht_col(int c, int j) { return j ^ (((c >> 3) & 3) << 2); }
 
-// Range-checked buffer view of one head's rows [r0, r_end) of a [T][H][128]
-// (or [T][H]) tensor: loads past the view (or before it, through a negative
-// row offset that wraps) return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_view(const void *base, size_t first_elem,
-                                                             int elt_bytes, int n_rows, size_t row_elems,
-                                                             int row_len) {
-    const char *b = static_cast<const char *>(base) + first_elem * elt_bytes;
-    const int bytes = n_rows > 0 ? static_cast<int>(((n_rows - 1) * row_elems + row_len) * elt_bytes) : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(b), static_cast<short>(0), bytes, 0x00020000);
+// Range-checked buffer view of n_rows rows of one head, starting at byte address
+// `base`, rows `row_bytes` apart, each `len_bytes` long: loads past the view (or
+// before it, through a negative offset that wraps) return zeros and stores past
+// it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_view(const char *base, int n_rows, uint32_t row_bytes,
+                                                             uint32_t len_bytes) {
+    const int bytes = n_rows > 0 ? static_cast<int>((n_rows - 1) * row_bytes + len_bytes) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), static_cast<short>(0), bytes, 0x00020000);
 }
 
 template <typename IO> struct BufLoad8;
@@ -245,6 +255,20 @@ template <> struct BufLoad8<float> {
         u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off + 16, 0, 0);
         return Raw{make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3])),
                    make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3]))};
+    }
+};
+
+template <typename OUT> struct OutStore;
+template <> struct OutStore<uint16_t> {
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *x) {
+        const uint4 w = Vec8<uint16_t>::pack(x);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w.x, w.y, w.z, w.w}, r, off, 0, 0);
+    }
+};
+template <> struct OutStore<float> {
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *x) {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])}, r, off + 16, 0, 0);
     }
 };
 
@@ -323,22 +347,35 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_kern
     typename Vec8<float>::Raw lar;
     float bet = 0.0f;
     typename IV::Raw graw;
+    // byte addresses of this (sequence, head)'s first row in each token-major tensor; a
+    // chunk's rows start C rows further per chunk, and offsets inside a chunk fit 32 bits
+    const uint32_t rowb_io = static_cast<uint32_t>(HD * sizeof(IO));
+    const uint32_t rowb_f = static_cast<uint32_t>(HD * 4);
+    const size_t first = static_cast<size_t>(t0) * HD + hD;
+    const char *qkv_base[3] = {static_cast<const char *>(p.q) + first * sizeof(IO),
+                               static_cast<const char *>(p.k) + first * sizeof(IO),
+                               static_cast<const char *>(p.v) + first * sizeof(IO)};
+    const char *la_base = reinterpret_cast<const char *>(p.log_alpha + first);
+    const char *beta_base = reinterpret_cast<const char *>(p.beta + static_cast<size_t>(t0) * H + h);
+    const char *g_base = p.epilogue ? static_cast<const char *>(p.g) + first * sizeof(IO) : nullptr;
+    char *o_base = static_cast<char *>(p.o) + first * sizeof(OUT);
+    const uint32_t off_io = static_cast<uint32_t>(et) * rowb_io + ec0 * sizeof(IO);
+    const uint32_t off_f = static_cast<uint32_t>(et) * rowb_f + ec0 * 4u;
+
     auto load_current = [&](int c) {
         const int r0 = c * C, nrow = min(L, r0 + C) - r0;
-        const uint32_t o_io = static_cast<uint32_t>(et * static_cast<int>(HD) + ec0) * sizeof(IO);
+        const size_t cio = static_cast<size_t>(r0) * rowb_io;
 #pragma unroll
         for (int s = 0; s < 3; ++s)
-            cur[s] = IB::load(rows_view(srcs[s], (t0 + r0) * HD + hD, sizeof(IO), nrow, HD, D), o_io);
-        lar = BufLoad8<float>::load(rows_view(p.log_alpha, (t0 + r0) * HD + hD, 4, nrow, HD, D),
-                                    static_cast<uint32_t>(et * static_cast<int>(HD) + ec0) * 4u);
+            cur[s] = IB::load(rows_view(qkv_base[s] + cio, nrow, rowb_io, D * sizeof(IO)), off_io);
+        lar = BufLoad8<float>::load(rows_view(la_base + static_cast<size_t>(r0) * rowb_f, nrow, rowb_f, D * 4), off_f);
         bet = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            rows_view(p.beta, (t0 + r0) * H + h, 4, nrow, H, 1), static_cast<uint32_t>(et * H) * 4u, 0, 0));
+            rows_view(beta_base + static_cast<size_t>(r0) * H * 4, nrow, H * 4, 4), static_cast<uint32_t>(et * H) * 4u, 0, 0));
     };
     auto load_gate = [&](int c) {
         const int r0 = c * C, nrow = min(L, r0 + C) - r0;
         if (p.epilogue)
-            graw = IB::load(rows_view(p.g, (t0 + r0) * HD + hD, sizeof(IO), nrow, HD, D),
-                            static_cast<uint32_t>(et * static_cast<int>(HD) + ec0) * sizeof(IO));
+            graw = IB::load(rows_view(g_base + static_cast<size_t>(r0) * rowb_io, nrow, rowb_io, D * sizeof(IO)), off_io);
     };
     if (nchunks > 0) {
         load_current(0);
@@ -515,33 +552,23 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_kern
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ba[i] = AF[ln * 17 + 4 * lh + i];
-                float sb[4], sa[4];  // S1 = I + B
+                // Only the a form of the sum is needed (T is an A operand).  Each operand is
+                // split into bf16 hi/lo once and reused by the products that read it.
+                float sa[4];  // a form of S1 = I + B
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sb[i] = bb[i] + ((4 * lh + i) == ln ? 1.0f : 0.0f);
-                    sa[i] = ba[i] + ((4 * lh + i) == ln ? 1.0f : 0.0f);
-                }
-                float b2b[4], b2a[4], t[4];
-                mm16(ba, bb, b2b);                      // B^2
-                mm16(bb, ba, b2a);
-                float b4b[4], b4a[4];
-                mm16(sa, b2b, t);                       // S2 = S1 + S1 B^2
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sb[i] += t[i];
-                mm16(b2b, sa, t);
+                for (int i = 0; i < 4; ++i) sa[i] = ba[i] + ((4 * lh + i) == ln ? 1.0f : 0.0f);
+                Split4 Ba(ba), Bb(bb);
+                Split4 B2b(mm16s(Ba, Bb)), B2a(mm16s(Bb, Ba));           // B^2
+                float t[4];
+                mm16s(B2b, Split4(sa), t);                                 // S2 = S1 + S1 B^2
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sa[i] += t[i];
-                mm16(b2a, b2b, b4b);                    // B^4
-                mm16(b2b, b2a, b4a);
-                mm16(sa, b4b, t);                       // S4 = S2 + S2 B^4
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sb[i] += t[i];
-                mm16(b4b, sa, t);
+                Split4 B4b(mm16s(B2a, B2b)), B4a(mm16s(B2b, B2a));       // B^4
+                mm16s(B4b, Split4(sa), t);                                 // S4 = S2 + S2 B^4
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sa[i] += t[i];
-                float b8b[4];
-                mm16(b4a, b4b, b8b);                    // B^8
-                mm16(b8b, sa, t);                       // a form of S8 = S4 + S4 B^8
+                Split4 B8b(mm16s(B4a, B4b));                               // B^8
+                mm16s(B8b, Split4(sa), t);                                 // S8 = S4 + S4 B^8
                 // T[m][k] = S8[m][k] beta_k: lane (m, g) stores row m, columns 4g .. 4g+3
                 float tv[4];
 #pragma unroll
@@ -653,7 +680,9 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_kern
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] = sigmoidf_(g[e]) * (o[e] * inv) * RW[ec0 + e];
             }
-            if (valid) OV::store(p.o, static_cast<size_t>(t0 + pos) * HD + hD + ec0, o);
+            OutStore<OUT>::store(rows_view(o_base + static_cast<size_t>(r0) * HD * sizeof(OUT), rend - r0,
+                                           static_cast<uint32_t>(HD * sizeof(OUT)), D * sizeof(OUT)),
+                                 static_cast<uint32_t>(et) * static_cast<uint32_t>(HD * sizeof(OUT)) + ec0 * sizeof(OUT), o);
         }
         if (ch + 1 < nchunks) load_gate(ch + 1);
         // the next chunk's first two barriers order these LDS reads before any rewrite

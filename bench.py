@@ -69,6 +69,91 @@ def cpu_info() -> str:
     return "unknown"
 
 
+KERNEL_SOURCES = {
+    "prefill": ["gated_delta_rule_kda_amd/csrc/kda_chunked.hip", "gated_delta_rule_kda_amd/csrc/kda_internal.h"],
+    "decode": ["gated_delta_rule_kda_amd/csrc/kda_recurrent.hip", "gated_delta_rule_kda_amd/csrc/kda_internal.h"],
+}
+
+
+def source_digest(paths) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(path: str) -> dict:
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+    (scaled by the same counters on a copy of known size), per kernel, kept only
+    while the kernel's sources hash to what they were when the counters were taken."""
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    out = {}
+    for kind, entry in rec.get("kernels", {}).items():
+        if kind in KERNEL_SOURCES and entry.get("source_sha256") == source_digest(KERNEL_SOURCES[kind]):
+            out[kind] = entry.get("hbm_bytes_per_launch")
+    return out
+
+
+def run_extra_workloads(kda, W, dev, stream, log) -> dict:
+    """Time the long-context (1 x 131072) and packed variable-length (64 sequences)
+    prefills: inputs generated one sequence at a time straight into device buffers."""
+    import torch
+    out = {}
+    for name in ("prefill_131072", "varlen_64"):
+        spec = W.workload(name)
+        lens = [int(x) for x in spec.lens]
+        N, H, T = len(lens), spec.heads, int(sum(lens))
+        bf = torch.bfloat16
+        bufs = {k: torch.empty((T, H, D), dtype=bf, device=dev) for k in ("q", "k", "v", "g")}
+        la = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+        beta = torch.empty((T, H), dtype=torch.float32, device=dev)
+        s0 = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+        t0 = time.perf_counter()
+        off = 0
+        cw = None
+        for n, L in enumerate(lens):
+            x = W.gen_prefill(W.PrefillSpec(lens=[L], heads=H, state_std=spec.state_std, seed=spec.seed,
+                                            first_seq=n))
+            for k in bufs:
+                bufs[k][off:off + L].copy_(torch.from_numpy(x[k]).to(bf))
+            la[off:off + L].copy_(torch.from_numpy(x["log_alpha"]))
+            beta[off:off + L].copy_(torch.from_numpy(x["beta"]))
+            s0[n].copy_(torch.from_numpy(x["state_in"][0]))
+            cw = x["conv_w"]
+            off += L
+        log(f"{name}: generated {T} tokens in {time.perf_counter() - t0:.1f}s")
+        cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
+        cwd = torch.from_numpy(cw).to(dev)
+        cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", prologue=True, epilogue=True)
+        o = torch.empty((T, H, D), dtype=bf, device=dev)
+        s_out = torch.empty_like(s0)
+        ws_n = kda.workspace_size(cfg, N, T)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+        def run():
+            kda.prefill(bufs["q"], bufs["k"], bufs["v"], la, beta, cu, g=bufs["g"], conv_w=cwd,
+                        state_in=s0, o=o, state_out=s_out, workspace=ws if ws_n else None, cfg=cfg,
+                        stream=stream, return_conv=False)
+
+        run()
+        torch.cuda.synchronize()
+        ms, med = time_events(run, 3, stream)
+        nb = prefill_algorithmic_bytes(T, H, N) + N * H * D * D * 4  # + the initial states read
+        out[name] = {"tokens": T, "sequences": N, "max_len": max(lens), "ms": ms,
+                     "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nb,
+                     "frac_of_hbm_roofline": nb / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}
+        log(f"{name}: {ms:.2f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+        del bufs, la, beta, s0, o, s_out
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_events(fn, steps: int, stream):
     """Mean ms of fn() over `steps` calls, from HIP events recorded on `stream`."""
     import torch
@@ -90,6 +175,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "recurrent"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run one fp32 device copy of this many MiB after the timed region "
+                         "(the known-size reference for HBM byte counters)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="counter-derived HBM bytes per launch, used while the kernel sources "
+                         "they were measured on are unchanged")
+    ap.add_argument("--extra-workloads", action="store_true",
+                    help="also time the 131072-token and the 64-sequence variable-length prefills")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the KDA core shards by head and by request with no "
@@ -172,6 +265,20 @@ def main() -> int:
     log(f"prefill {pre_mean:.3f} ms (median {pre_med:.3f}); decode {dec_mean:.4f} ms "
         f"(median {dec_med:.4f}); wall {wall:.2f}s")
 
+    copy_cal = None
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        xs = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        ys = torch.empty_like(xs)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        ys.copy_(xs)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        copy_cal = {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ev0.elapsed_time(ev1)}
+        del xs, ys
+
     tok_s = T / (pre_mean * 1e-3)
     pb = prefill_algorithmic_bytes(T, H, N)
     pf = prefill_mfma_flops(T, H)
@@ -200,6 +307,9 @@ def main() -> int:
                          f"fp64, {ct:.1f}s wall on {threads} threads ({cpu_info()})"}
         log(f"oracle: {L0} tokens x {H} heads in {ct:.1f}s on {threads} threads")
 
+    traffic = load_traffic(args.traffic)
+    extra = run_extra_workloads(kda, W, dev, stream, log) if args.extra_workloads else None
+
     res = {
         "metric": "KDA prefill tokens/sec (H=96,d=128) + decode state GB/s at B=256",
         "value": tok_s,
@@ -227,12 +337,16 @@ def main() -> int:
                    "frac_of_hbm_peak": dec_gbps / HBM_PEAK_GBPS},
         "roofline": {"kernel": f"prefill ({algo_name})", "bound": "hbm", "achieved": pre_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": pre_gbps / HBM_PEAK_GBPS,
-                     "traffic": None},
+                     "traffic": traffic.get("prefill")},
         "roofline_decode": {"kernel": "decode step", "bound": "hbm", "achieved": dec_gbps,
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dec_gbps / HBM_PEAK_GBPS,
-                            "traffic": None},
+                            "traffic": traffic.get("decode")},
         "cpu_baseline": cpu,
     }
+    if copy_cal:
+        res["copy_calibration"] = copy_cal
+    if extra:
+        res["extra_workloads"] = extra
     print(json.dumps(res), flush=True)
     return 0
 

@@ -72,6 +72,7 @@ class PrefillSpec:
     unit_qk: bool = False          # normalise q, k per (token, head) (prologue off)
     seed: int = 1
     name: str = "custom"
+    first_seq: int = 0             # index of the first sequence in the seed space (slices of a larger workload)
 
     @property
     def total(self) -> int:
@@ -79,7 +80,7 @@ class PrefillSpec:
 
 
 def _fill_blocks(out: np.ndarray, seed: int, tensor: int, cu: np.ndarray, draw,
-                 bf16: bool = False, per_head: bool = True) -> None:
+                 bf16: bool = False, per_head: bool = True, n0: int = 0) -> None:
     """out[cu[n]:cu[n+1], h] for every (sequence n, head h) from its own generator
     (or out[cu[n]:cu[n+1]] for every sequence n from one generator when
     per_head is False), rounded to bf16 values when asked.  Workers write
@@ -93,10 +94,10 @@ def _fill_blocks(out: np.ndarray, seed: int, tensor: int, cu: np.ndarray, draw,
         n, h = job
         s, e = int(cu[n]), int(cu[n + 1])
         if h is None:
-            blk = draw(_rng(seed, tensor, n, H), (e - s,) + out.shape[1:])
+            blk = draw(_rng(seed, tensor, n0 + n, H), (e - s,) + out.shape[1:])
             out[s:e] = _bf16_inplace(blk) if bf16 else blk
             return
-        blk = draw(_rng(seed, tensor, n, h), (e - s,) + out.shape[2:])
+        blk = draw(_rng(seed, tensor, n0 + n, h), (e - s,) + out.shape[2:])
         if bf16:
             blk = _bf16_inplace(blk)
         out[s:e, h] = blk
@@ -155,35 +156,36 @@ def gen_prefill(spec: PrefillSpec) -> Dict[str, np.ndarray]:
     cu[1:] = np.cumsum(lens)
     T, H, N = int(cu[-1]), spec.heads, len(lens)
     sd = spec.seed
+    n0 = spec.first_seq
     out: Dict[str, np.ndarray] = {"cu_seqlens": cu.astype(np.int32)}
     for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V)):
         a = np.empty((T, H, D), np.float32)
         draw = _unit if (spec.unit_qk and name != "v") else _normal32
-        _fill_blocks(a, sd, tid, cu, draw, bf16=spec.io == "bf16")
+        _fill_blocks(a, sd, tid, cu, draw, bf16=spec.io == "bf16", n0=n0)
         out[name] = a
     if spec.epilogue:
         a = np.empty((T, H, D), np.float32)
-        _fill_blocks(a, sd, T_G, cu, _normal32, bf16=spec.io == "bf16")
+        _fill_blocks(a, sd, T_G, cu, _normal32, bf16=spec.io == "bf16", n0=n0)
         out["g"] = a
     a = np.empty((T, H, D), np.float32)
-    _fill_blocks(a, sd, T_ALPHA, cu, _log_alpha(spec.decay))
+    _fill_blocks(a, sd, T_ALPHA, cu, _log_alpha(spec.decay), n0=n0)
     out["log_alpha"] = a
     b = np.empty((T, H), np.float32)
-    _fill_blocks(b, sd, T_BETA, cu, _beta)
+    _fill_blocks(b, sd, T_BETA, cu, _beta, n0=n0)
     out["beta"] = b
     if spec.prologue:
         out["conv_w"] = (_rng(sd, T_CONVW).standard_normal((3, H * D, 4)) * 0.5).astype(np.float32)
         if spec.conv_in:
             ci = np.empty((N, 3, 3, H * D), np.float32)
             for n in range(N):
-                ci[n] = _rng(sd, T_CONVIN, n).standard_normal((3, 3, H * D), dtype=np.float32)
+                ci[n] = _rng(sd, T_CONVIN, n0 + n).standard_normal((3, 3, H * D), dtype=np.float32)
             out["conv_in"] = ci
     if spec.state_std is not None:
         st = np.empty((N, H, D, D), np.float32)
 
         def one(nh):
             n, h = nh
-            st[n, h] = _rng(sd, T_STATE, n, h).standard_normal((D, D)) * spec.state_std
+            st[n, h] = _rng(sd, T_STATE, n0 + n, h).standard_normal((D, D)) * spec.state_std
 
         with ThreadPoolExecutor(_workers()) as ex:
             list(ex.map(one, [(n, h) for n in range(N) for h in range(H)]))

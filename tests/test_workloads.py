@@ -47,3 +47,12 @@ def test_varlen_lengths():
     # distribution mean 8192 for sigma = 1 (checked on many draws, not the 64 used)
     many = W.varlen_lengths(n_seqs=200000, lo=0, hi=10 ** 9, seed=11)
     assert abs(np.mean(many) / 8192.0 - 1.0) < 0.03
+
+
+def test_sequence_slices_of_a_larger_workload():
+    # a workload can be generated one sequence at a time (first_seq), matching the whole
+    a = W.gen_prefill(W.PrefillSpec(lens=[40, 25, 10], heads=3, state_std=0.02, seed=9))
+    b = W.gen_prefill(W.PrefillSpec(lens=[25], heads=3, state_std=0.02, seed=9, first_seq=1))
+    for key in ("q", "k", "v", "g", "log_alpha", "beta"):
+        assert np.array_equal(a[key][40:65], b[key]), key
+    assert np.array_equal(a["state_in"][1], b["state_in"][0])

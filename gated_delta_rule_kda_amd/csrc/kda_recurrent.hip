@@ -28,6 +28,7 @@ namespace kda {
 namespace {
 
 constexpr int THREADS = 256;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
@@ -81,8 +82,9 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
         const float4 *src = reinterpret_cast<const float4 *>(p.state_in + sbase);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float4 x = src[((i0 + r) * D + j0) / 4];
-            S[r][0] = x.x; S[r][1] = x.y; S[r][2] = x.z; S[r][3] = x.w;
+            // the state is streamed: read once, written once, no reuse through the caches
+            const f32x4v x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(&src[((i0 + r) * D + j0) / 4]));
+            S[r][0] = x[0]; S[r][1] = x[1]; S[r][2] = x[2]; S[r][3] = x[3];
         }
     } else {
 #pragma unroll
@@ -243,8 +245,10 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
     if (p.state_out) {
         float4 *dst = reinterpret_cast<float4 *>(p.state_out + sbase);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            dst[((i0 + r) * D + j0) / 4] = make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
+        for (int r = 0; r < 16; ++r) {
+            const f32x4v y = {S[r][0], S[r][1], S[r][2], S[r][3]};
+            __builtin_nontemporal_store(y, reinterpret_cast<f32x4v *>(&dst[((i0 + r) * D + j0) / 4]));
+        }
     }
     if (p.prologue && p.conv_out) {
         const size_t base = static_cast<size_t>(srow) * 3 * CONV_HIST * HD + h * D + c;

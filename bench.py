@@ -173,7 +173,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--algo", default="auto", choices=["auto", "chunked", "recurrent"])
+    ap.add_argument("--algo", default="auto",
+                    choices=["auto", "recurrent", "chunked", "chunked_throughput", "chunked_latency"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one fp32 device copy of this many MiB after the timed region "
@@ -287,9 +288,7 @@ def main() -> int:
     state_bytes = 2 * B * H * D * D * 4
     dec_state_gbps = state_bytes / (dec_mean * 1e-3) / 1e9
     dec_gbps = db / (dec_mean * 1e-3) / 1e9
-    algo_name = {0: "auto", 1: "recurrent", 2: "chunked"}[cfg.algo]
-    if algo_name == "auto":
-        algo_name = kda.resolved_algo(cfg)
+    algo_name = kda.resolved_algo(cfg, N)
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 HEAD_DIM = 128
 F32, BF16 = 0, 1
-ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2}
+ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2, "chunked_throughput": 3, "chunked_latency": 4}
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 
 EXPORTS = ("kda_config_init", "kda_prefill_workspace_size", "kda_prefill",
@@ -80,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill_workspace_size.restype = ctypes.c_int32
         L.kda_prefill.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(PrefillArgs), _vp]
         L.kda_prefill.restype = ctypes.c_int32
-        L.kda_prefill_resolved_algo.argtypes = [ctypes.POINTER(Config)]
+        L.kda_prefill_resolved_algo.argtypes = [ctypes.POINTER(Config), ctypes.c_int32]
         L.kda_prefill_resolved_algo.restype = ctypes.c_int32
         L.kda_decode_step.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(DecodeArgs), _vp]
         L.kda_decode_step.restype = ctypes.c_int32
@@ -254,9 +254,10 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
     return o
 
 
-def resolved_algo(cfg: Config) -> str:
-    """Name of the prefill algorithm the library runs for `cfg` (AUTO resolved)."""
-    code = lib().kda_prefill_resolved_algo(ctypes.byref(cfg))
+def resolved_algo(cfg: Config, num_seqs: int = 1) -> str:
+    """Name of the prefill algorithm the library runs for `cfg` and `num_seqs` sequences
+    on the current device (AUTO and CHUNKED resolved)."""
+    code = lib().kda_prefill_resolved_algo(ctypes.byref(cfg), num_seqs)
     if code < 0:
         raise KdaError(ERR_INVALID_ARGUMENT, "invalid configuration")
     return {v: k for k, v in ALGOS.items()}[code]

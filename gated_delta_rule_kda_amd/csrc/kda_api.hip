@@ -32,6 +32,8 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t *cu, int32_t n
     order[rank] = i;
 }
 
+bool valid_algo(int32_t a) { return a >= KDA_ALGO_AUTO && a <= KDA_ALGO_CHUNKED_LATENCY; }
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool trace_enabled() {
@@ -50,8 +52,7 @@ kda_status check_config(const kda_config *cfg) {
     if (cfg->out_dtype != KDA_DTYPE_F32 && cfg->out_dtype != KDA_DTYPE_BF16) return KDA_ERR_INVALID_ARGUMENT;
     if ((cfg->prologue != 0 && cfg->prologue != 1) || (cfg->epilogue != 0 && cfg->epilogue != 1))
         return KDA_ERR_INVALID_ARGUMENT;
-    if (cfg->algo != KDA_ALGO_AUTO && cfg->algo != KDA_ALGO_RECURRENT && cfg->algo != KDA_ALGO_CHUNKED)
-        return KDA_ERR_INVALID_ARGUMENT;
+    if (!valid_algo(cfg->algo)) return KDA_ERR_INVALID_ARGUMENT;
     if (!isfinite(cfg->scale) || !(cfg->l2_eps >= 0.f) || !(cfg->rms_eps >= 0.f) ||
         !isfinite(cfg->l2_eps) || !isfinite(cfg->rms_eps))
         return KDA_ERR_INVALID_ARGUMENT;
@@ -67,6 +68,18 @@ bool ok_ptr(const void *p, bool required) {
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
 }  // namespace
+
+int device_cu_count() {
+    constexpr int MAX_DEV = 64;
+    static int cached[MAX_DEV] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < MAX_DEV && cached[dev] > 0) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev < MAX_DEV) cached[dev] = cus;
+    return cus;
+}
 
 size_t order_workspace_bytes(int32_t n) {
     if (n <= 1 || n > ORDER_MAX_SEQS) return 0;
@@ -98,10 +111,17 @@ void kda_config_init(kda_config *cfg, int32_t num_heads) {
     cfg->rms_eps = 1e-6f;
 }
 
-int32_t kda_prefill_resolved_algo(const kda_config *cfg) {
-    if (check_config(cfg) != KDA_OK) return -1;
-    if (cfg->algo != KDA_ALGO_AUTO) return cfg->algo;
-    return cfg->io_dtype == KDA_DTYPE_BF16 ? KDA_ALGO_CHUNKED : KDA_ALGO_RECURRENT;
+int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs) {
+    if (check_config(cfg) != KDA_OK || num_seqs <= 0) return -1;
+    int algo = cfg->algo;
+    if (algo == KDA_ALGO_AUTO) algo = cfg->io_dtype == KDA_DTYPE_BF16 ? KDA_ALGO_CHUNKED : KDA_ALGO_RECURRENT;
+    if (algo == KDA_ALGO_CHUNKED) {
+        // more (sequence, head) items than CUs: two workgroups per CU keep the CU busy;
+        // otherwise each item's chain of chunks is the critical path: pipeline it
+        const int64_t items = static_cast<int64_t>(num_seqs) * cfg->num_heads;
+        algo = items > device_cu_count() ? KDA_ALGO_CHUNKED_THROUGHPUT : KDA_ALGO_CHUNKED_LATENCY;
+    }
+    return algo;
 }
 
 kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens,
@@ -130,7 +150,7 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     const size_t need = order_workspace_bytes(a->num_seqs);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
 
-    const int algo = kda_prefill_resolved_algo(cfg);
+    const int algo = kda_prefill_resolved_algo(cfg, a->num_seqs);
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     int32_t *order = need > 0 ? static_cast<int32_t *>(a->workspace) : nullptr;
@@ -156,8 +176,13 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
         fprintf(stderr, "[kda] prefill N=%d H=%d T=%lld io=%d out=%d algo=%d prologue=%d epilogue=%d\n",
                 a->num_seqs, cfg->num_heads, static_cast<long long>(a->total_tokens), cfg->io_dtype,
                 cfg->out_dtype, algo, cfg->prologue, cfg->epilogue);
-    hipError_t e = algo == KDA_ALGO_CHUNKED ? launch_chunked(p, cfg->io_dtype, cfg->out_dtype, s)
-                                            : launch_recurrent(p, cfg->io_dtype, cfg->out_dtype, s);
+    hipError_t e;
+    if (algo == KDA_ALGO_CHUNKED_THROUGHPUT)
+        e = launch_chunked_throughput(p, cfg->io_dtype, cfg->out_dtype, s);
+    else if (algo == KDA_ALGO_CHUNKED_LATENCY)
+        e = launch_chunked_latency(p, cfg->io_dtype, cfg->out_dtype, s);
+    else
+        e = launch_recurrent(p, cfg->io_dtype, cfg->out_dtype, s);
     return from_hip(e);
 }
 

@@ -1,0 +1,213 @@
+// kda_chunk_common.h -- operand helpers shared by the chunked prefill kernels
+// (kda_chunked.hip and kda_chunked_pipe.hip): chunk geometry, bf16 hi/lo
+// operand splits, the gfx950 MFMA wrappers, the K-slot permutation that lets
+// accumulator tiles serve as B operands, and range-checked buffer views.
+#pragma once
+
+#include "kda_internal.h"
+
+namespace kda {
+namespace chunk {
+
+constexpr int C = 16;          // tokens per chunk
+constexpr int OPK = D + 8;     // padded row (bf16 elements) of [16][128] operand planes
+constexpr int OPT = C + 4;     // padded row of [*][16] operand planes
+constexpr int FPK = D + 4;     // padded row (floats) of [16][128] fp32 tiles
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int PL_CD = C * OPK;           // bf16 elements of one [16][128] plane
+constexpr int PL_DC = D * OPT;           // one [128][16] plane
+constexpr int PL_CC = C * OPT;           // one [16][16] plane
+
+// Position of K index j (0..31) inside a 32-wide K block of an A operand
+// whose B operand comes from two stacked accumulator tiles: B slot 8h + i
+// holds row 16(i/4) + 4h + (i%4), so true index j goes to slot
+// ((j>>2)&3)*8 + ((j>>4)&1)*4 + (j&3).
+__device__ __forceinline__ int kperm(int j) {
+    return ((j & 12) << 1) | ((j & 16) >> 2) | (j & 3);
+}
+
+// Round-to-nearest-even bf16 split of two floats: x = hi + lo + O(2^-18 |x|).
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    f32x2_t x = {a, b};
+    uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+    f32x2_t r = {a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u)};
+    hi = h;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+}
+
+__device__ __forceinline__ void split8(const float *x, uint4 &hi, uint4 &lo) {
+    split2(x[0], x[1], hi.x, lo.x);
+    split2(x[2], x[3], hi.y, lo.y);
+    split2(x[4], x[5], hi.z, lo.z);
+    split2(x[6], x[7], hi.w, lo.w);
+}
+
+__device__ __forceinline__ void split1(float a, uint16_t &hi, uint16_t &lo) {
+    uint32_t h, l;
+    split2(a, 0.0f, h, l);
+    hi = static_cast<uint16_t>(h);
+    lo = static_cast<uint16_t>(l);
+}
+
+__device__ __forceinline__ void split4(const float *x, uint2 &hi, uint2 &lo) {
+    split2(x[0], x[1], hi.x, lo.x);
+    split2(x[2], x[3], hi.y, lo.y);
+}
+
+__device__ __forceinline__ f32x4_t mma16(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a),
+                                                     __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
+}
+
+// (a_hi + a_lo)(b_hi + b_lo) without the lo*lo term, K = 16.
+__device__ __forceinline__ f32x4_t mma16_3(uint2 ahi, uint2 alo, uint2 bhi, uint2 blo, f32x4_t c) {
+    c = mma16(alo, bhi, c);
+    c = mma16(ahi, blo, c);
+    return mma16(ahi, bhi, c);
+}
+
+// A 16x16 fp32 matrix fragment (4 values per lane) split into bf16 hi/lo.
+struct Split4 {
+    uint2 h, l;
+    __device__ __forceinline__ explicit Split4(const float *x) { split4(x, h, l); }
+    __device__ __forceinline__ explicit Split4(const f32x4_t &x) {
+        const float v[4] = {x[0], x[1], x[2], x[3]};
+        split4(v, h, l);
+    }
+};
+
+// x y for 16x16 matrices held as (a form of x, b form of y), on a fresh accumulator.
+__device__ __forceinline__ f32x4_t mm16s(const Split4 &xa, const Split4 &yb) {
+    return mma16_3(xa.h, xa.l, yb.h, yb.l, f32x4_t{0.f, 0.f, 0.f, 0.f});
+}
+__device__ __forceinline__ void mm16s(const Split4 &xa, const Split4 &yb, float *d) {
+    const f32x4_t r = mm16s(xa, yb);
+    d[0] = r[0]; d[1] = r[1]; d[2] = r[2]; d[3] = r[3];
+}
+
+__device__ __forceinline__ f32x4_t mma(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// (a_hi + a_lo)(b_hi + b_lo) without the lo*lo term.
+__device__ __forceinline__ f32x4_t mma3(uint4 ahi, uint4 alo, uint4 bhi, uint4 blo, f32x4_t c) {
+    c = mma(alo, bhi, c);
+    c = mma(ahi, blo, c);
+    return mma(ahi, bhi, c);
+}
+
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// Eight consecutive io values starting at element i (i a multiple of 8): a raw
+// 16- or 32-byte load, and its conversion to fp32, kept apart so that a batch
+// of loads can be issued before any of them is consumed.
+template <typename IO> struct Vec8;
+template <> struct Vec8<uint16_t> {
+    struct Raw { uint4 u; };
+    static __device__ __forceinline__ Raw raw(const void *p, size_t i) {
+        return Raw{*reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + i)};
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *x) {
+        const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(w[e] << 16);
+            x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void load(const void *p, size_t i, float *x) { unpack(raw(p, i), x); }
+    static __device__ __forceinline__ uint4 pack(const float *x) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x[2 * e], x[2 * e + 1]}, bf16x2_t));
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    static __device__ __forceinline__ void store(void *p, size_t i, const float *x) {
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p) + i) = pack(x);
+    }
+};
+template <> struct Vec8<float> {
+    struct Raw { float4 a, b; };
+    static __device__ __forceinline__ Raw raw(const void *p, size_t i) {
+        const float4 *q = reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+        return Raw{q[0], q[1]};
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *x) {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+    }
+    static __device__ __forceinline__ void load(const void *p, size_t i, float *x) { unpack(raw(p, i), x); }
+    static __device__ __forceinline__ void store(void *p, size_t i, const float *x) {
+        float4 *q = reinterpret_cast<float4 *>(static_cast<float *>(p) + i);
+        q[0] = make_float4(x[0], x[1], x[2], x[3]);
+        q[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+};
+
+// Storage column of key channel c in a channel-permuted [*][128] plane.
+__device__ __forceinline__ int cperm(int c) { return (c & ~31) | kperm(c & 31); }
+
+// Column swizzle of the Khat^T planes: row c keeps its 4-token groups
+// contiguous (8-byte MFMA operand reads) but XORs the group index with
+// (c / 8) % 4, spreading the transposed stores of 16 lanes (rows 8 apart)
+// over four bank groups.
+__device__ __forceinline__ int kht_col(int c, int j) { return j ^ (((c >> 3) & 3) << 2); }
+
+// Range-checked buffer view of n_rows rows of one head, starting at byte address
+// `base`, rows `row_bytes` apart, each `len_bytes` long: loads past the view (or
+// before it, through a negative offset that wraps) return zeros and stores past
+// it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_view(const char *base, int n_rows, uint32_t row_bytes,
+                                                             uint32_t len_bytes) {
+    const int bytes = n_rows > 0 ? static_cast<int>((n_rows - 1) * row_bytes + len_bytes) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+
+template <typename IO> struct BufLoad8;
+template <> struct BufLoad8<uint16_t> {
+    using Raw = typename Vec8<uint16_t>::Raw;
+    static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+        u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+        return Raw{make_uint4(v[0], v[1], v[2], v[3])};
+    }
+};
+template <> struct BufLoad8<float> {
+    using Raw = typename Vec8<float>::Raw;
+    static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+        u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+        u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off + 16, 0, 0);
+        return Raw{make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3])),
+                   make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3]))};
+    }
+};
+
+template <typename OUT> struct OutStore;
+template <> struct OutStore<uint16_t> {
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *x) {
+        const uint4 w = Vec8<uint16_t>::pack(x);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{w.x, w.y, w.z, w.w}, r, off, 0, 0);
+    }
+};
+template <> struct OutStore<float> {
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *x) {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])}, r, off + 16, 0, 0);
+    }
+};
+
+}  // namespace chunk
+}  // namespace kda

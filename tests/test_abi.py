@@ -132,3 +132,18 @@ def test_decode_rejects_bad_arguments():
     assert dec(kda.config(4), batch=0) == kda.ERR_INVALID_ARGUMENT
     assert dec(kda.config(4), slots=FAKE + 4) == kda.ERR_INVALID_ARGUMENT
     assert dec(kda.config(4, head_dim=256)) == kda.ERR_UNSUPPORTED
+
+
+def test_resolved_algo():
+    # fp32 io -> the recurrent reference path; explicit choices pass through;
+    # invalid configurations and sequence counts -> -1
+    L = kda.lib()
+    c = kda.config(4, io_dtype="f32")
+    assert kda.resolved_algo(c, 3) == "recurrent"
+    for name in ("recurrent", "chunked_throughput", "chunked_latency"):
+        assert kda.resolved_algo(kda.config(4, algo=name), 2) == name
+    assert kda.resolved_algo(kda.config(8), 1) in ("chunked_throughput", "chunked_latency")
+    assert L.kda_prefill_resolved_algo(ctypes.byref(kda.config(4)), 0) == -1
+    bad = kda.config(4)
+    bad.algo = 9
+    assert L.kda_prefill_resolved_algo(ctypes.byref(bad), 1) == -1

@@ -18,6 +18,10 @@ pytestmark = pytest.mark.gpu
 BF16_TOL = 1e-2
 CHUNKED_RAW_TOL = 2e-3
 
+# both chunked kernels: two 4-wave workgroups per CU, and the 8-wave producer/consumer pipeline
+VARIANTS = ["chunked_throughput", "chunked_latency"]
+variants = pytest.mark.parametrize("algo", VARIANTS)
+
 
 def _check(g, r, out, tol=BF16_TOL, conv=True):
     eo = err(g["o"], r["o"]) if out == "f32" else err_bf16(g["o"], r["o"])
@@ -30,51 +34,56 @@ def _check(g, r, out, tol=BF16_TOL, conv=True):
     return eo, es
 
 
-def test_core_recurrence_unit_keys():
+@variants
+def test_core_recurrence_unit_keys(algo):
     """B=1, H=2, T=256 core recurrence (fp32 io, no prologue/epilogue) on the chunked path."""
     inp = W.gen_prefill(W.workload("core_fp32"))
     say("chunked core_fp32")
-    g = gpu_prefill(inp, io="f32", out="f32", algo="chunked")
+    g = gpu_prefill(inp, io="f32", out="f32", algo=algo)
     r = oracle_prefill(inp)
     _check(g, r, "f32", tol=CHUNKED_RAW_TOL)
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_full_layer_ragged(out):
+@variants
+def test_full_layer_ragged(out, algo):
     """Several chunks with ragged tails, random S0 and conv history, bf16 io."""
     spec = W.PrefillSpec(lens=[5, 64, 130, 1, 33, 0, 97], heads=4, state_std=0.02, conv_in=True, seed=41)
     inp = W.gen_prefill(spec)
     say(f"chunked full layer ragged out={out}")
-    g = gpu_prefill(inp, io="bf16", out=out, algo="chunked")
+    g = gpu_prefill(inp, io="bf16", out=out, algo=algo)
     r = oracle_prefill(inp)
     _check(g, r, out)
 
 
-def test_full_layer_slow_decay():
+@variants
+def test_full_layer_slow_decay(algo):
     """Slow decay (memory ~50 tokens) carries S0 and the inter-chunk state far."""
     spec = W.PrefillSpec(lens=[300, 77], heads=3, state_std=0.02, conv_in=True, decay="slow", seed=42)
     inp = W.gen_prefill(spec)
     say("chunked slow decay")
-    g = gpu_prefill(inp, io="bf16", out="f32", algo="chunked")
+    g = gpu_prefill(inp, io="bf16", out="f32", algo=algo)
     r = oracle_prefill(inp)
     _check(g, r, "f32")
 
 
-def test_raw_read_precision_slow_decay():
+@variants
+def test_raw_read_precision_slow_decay(algo):
     """No epilogue: the raw read o~ and S from the chunked kernel's split-bf16 arithmetic."""
     spec = W.PrefillSpec(lens=[200, 45], heads=2, state_std=0.02, conv_in=True, decay="slow",
                          epilogue=False, seed=43)
     inp = W.gen_prefill(spec)
-    g = gpu_prefill(inp, io="bf16", out="f32", algo="chunked")
+    g = gpu_prefill(inp, io="bf16", out="f32", algo=algo)
     r = oracle_prefill(inp)
     _check(g, r, "f32", tol=CHUNKED_RAW_TOL)
 
 
-def test_edge_lengths():
+@variants
+def test_edge_lengths(algo):
     lens = [0, 1, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 0]
     inp = W.gen_prefill(W.PrefillSpec(lens=lens, heads=2, state_std=0.05, conv_in=True, seed=44))
     say("chunked edge lengths")
-    g = gpu_prefill(inp, io="bf16", out="f32", algo="chunked")
+    g = gpu_prefill(inp, io="bf16", out="f32", algo=algo)
     r = oracle_prefill(inp)
     _check(g, r, "f32")
     # zero-length sequences pass state and conv history through unchanged
@@ -82,23 +91,26 @@ def test_edge_lengths():
     assert np.array_equal(g["state"][-1], inp["state_in"][-1].astype(np.float64))
 
 
-def test_in_place_state_and_conv():
+@variants
+def test_in_place_state_and_conv(algo):
     inp = W.gen_prefill(W.PrefillSpec(lens=[70, 9, 2], heads=2, state_std=0.05, conv_in=True, seed=45))
     r = oracle_prefill(inp)
-    g = gpu_prefill(inp, io="bf16", out="f32", algo="chunked", in_place=True)
+    g = gpu_prefill(inp, io="bf16", out="f32", algo=algo, in_place=True)
     _check(g, r, "f32")
 
 
-def test_fp32_io_with_gain():
+@variants
+def test_fp32_io_with_gain(algo):
     spec = W.PrefillSpec(lens=[45, 7], heads=3, io="f32", state_std=0.05, conv_in=True, seed=46)
     inp = W.gen_prefill(spec)
     rw = np.random.default_rng(5).uniform(0.5, 1.5, 128).astype(np.float32)
-    g = gpu_prefill(inp, io="f32", out="f32", algo="chunked", rms_w=rw)
+    g = gpu_prefill(inp, io="f32", out="f32", algo=algo, rms_w=rw)
     r = oracle_prefill(inp, rms_w=rw)
     _check(g, r, "f32")
 
 
-def test_orthonormal_keys_store_all():
+@variants
+def test_orthonormal_keys_store_all(algo):
     """alpha = 1, beta = 1, S0 = 0 and 128 orthonormal keys: S = K^T V exactly,
     and every key reads back its own value (crosstalk-free delta writes)."""
     import torch
@@ -112,7 +124,7 @@ def test_orthonormal_keys_store_all():
     inp = {"cu_seqlens": np.array([0, T], np.int32), "q": K[:, None, :], "k": K[:, None, :],
            "v": V[:, None, :], "log_alpha": np.zeros((T, 1, 128), np.float32),
            "beta": np.ones((T, 1), np.float32)}
-    g = gpu_prefill(inp, io="f32", out="f32", algo="chunked", prologue=False, epilogue=False)
+    g = gpu_prefill(inp, io="f32", out="f32", algo=algo, prologue=False, epilogue=False)
     S = g["state"][0, 0]
     ref = K.astype(np.float64).T @ V.astype(np.float64)
     e = err(S, ref)
@@ -122,7 +134,8 @@ def test_orthonormal_keys_store_all():
     assert err(g["o"][:, 0] * np.sqrt(128.0), V) <= CHUNKED_RAW_TOL
 
 
-def test_chaining_matches_one_call():
+@variants
+def test_chaining_matches_one_call(algo):
     """prefill(a) then prefill(b) from the returned state and conv cache equals prefill(a|b)."""
     import torch
     spec = W.PrefillSpec(lens=[150], heads=2, state_std=0.02, conv_in=True, seed=48)
@@ -130,12 +143,12 @@ def test_chaining_matches_one_call():
     cut = 77
     a = {k: (v[:cut] if k in ("q", "k", "v", "g", "log_alpha", "beta") else v) for k, v in full.items()}
     a["cu_seqlens"] = np.array([0, cut], np.int32)
-    ga = gpu_prefill(a, io="bf16", out="f32", algo="chunked")
+    ga = gpu_prefill(a, io="bf16", out="f32", algo=algo)
     b = {k: (v[cut:] if k in ("q", "k", "v", "g", "log_alpha", "beta") else v) for k, v in full.items()}
     b["cu_seqlens"] = np.array([0, 150 - cut], np.int32)
     b["state_in"] = ga["state"].astype(np.float32)
     b["conv_in"] = ga["conv"].astype(np.float32)
-    gb = gpu_prefill(b, io="bf16", out="f32", algo="chunked")
+    gb = gpu_prefill(b, io="bf16", out="f32", algo=algo)
     r = oracle_prefill(full)
     o = np.concatenate([ga["o"], gb["o"]])
     assert err(o, r["o"]) <= BF16_TOL
@@ -143,14 +156,15 @@ def test_chaining_matches_one_call():
     assert np.array_equal(gb["conv"], r["conv"])
 
 
-def test_varlen_subset():
+@variants
+def test_varlen_subset(algo):
     """Eight sequences drawn from the packed variable-length workload's length
     distribution (lognormal, mean 8192, clipped to [16, 65536]), 2 heads."""
     lens = W.varlen_lengths(n_seqs=8, seed=49)
     lens = [min(l, 6000) for l in lens]
     inp = W.gen_prefill(W.PrefillSpec(lens=lens, heads=2, state_std=0.02, seed=49))
     say(f"chunked varlen subset lens={lens}")
-    g = gpu_prefill(inp, io="bf16", out="bf16", algo="chunked")
+    g = gpu_prefill(inp, io="bf16", out="bf16", algo=algo)
     r = oracle_prefill(inp)
     _check(g, r, "bf16")
 
@@ -164,7 +178,9 @@ def test_full_size_prefill_sampled():
     inp = W.gen_prefill(spec)
     say("prefill_4x4096: gpu")
     g = gpu_prefill(inp, io="bf16", out="bf16", algo="auto")
-    assert kda.resolved_algo(kda.config(96)) == "chunked"
+    # 384 (sequence, head) items on 256 CUs: the throughput variant; 96 items: the pipeline
+    assert kda.resolved_algo(kda.config(96), 4) == "chunked_throughput"
+    assert kda.resolved_algo(kda.config(96), 1) == "chunked_latency"
     for seqs, heads in (([0], [0, 57]), ([3], [95])):
         sub = subset(inp, seqs, heads)
         r = oracle_prefill(sub)
@@ -172,4 +188,23 @@ def test_full_size_prefill_sampled():
         say(f"  seqs {seqs} heads {heads}")
         _check(gs, r, "bf16")
     # every output is finite
+    assert np.isfinite(g["o"]).all() and np.isfinite(g["state"]).all()
+
+
+def test_long_context_sampled():
+    """One 131072-token sequence, 96 heads, random fp32 S0 (the long-context launch, which
+    resolves to the pipelined variant): sampled heads against the oracle."""
+    import gated_delta_rule_kda_amd as kda
+    spec = W.workload("prefill_131072")
+    say("prefill_131072: generating inputs")
+    inp = W.gen_prefill(spec)
+    say("prefill_131072: gpu")
+    g = gpu_prefill(inp, io="bf16", out="bf16", algo="auto")
+    assert kda.resolved_algo(kda.config(96), 1) == "chunked_latency"
+    heads = [3, 77]
+    sub = subset(inp, [0], heads)
+    r = oracle_prefill(sub)
+    gs = gpu_rows(g, inp, [0], heads)
+    say(f"  heads {heads}")
+    _check(gs, r, "bf16")
     assert np.isfinite(g["o"]).all() and np.isfinite(g["state"]).all()

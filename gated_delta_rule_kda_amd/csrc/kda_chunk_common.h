@@ -104,6 +104,31 @@ __device__ __forceinline__ f32x4_t mma3(uint4 ahi, uint4 alo, uint4 bhi, uint4 b
     return mma(ahi, bhi, c);
 }
 
+// A copy of x that the compiler cannot see through: values derived from it are
+// recomputed where they are used instead of being hoisted out of a loop and kept
+// live (or spilled) across it.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// Sum over each half wave (lanes 0-31 and 32-63 separately), returned to every lane of
+// the half: two quad permutes, the half-row and row mirrors (DPP operands of the adds)
+// and one ds_swizzle that exchanges the two 16-lane rows of the half.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float half_wave_sum(float x) {
+    x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+    x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+    x += dpp<0x141>(x);  // row_half_mirror: quad sums of the two halves of each 8 lanes
+    x += dpp<0x140>(x);  // row_mirror: the two 8-lane halves of each 16-lane row
+    // bit-mask swizzle inside 32 lanes: and 0x1f, or 0, xor 0x10
+    x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+    return x;
+}
+
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
@@ -206,6 +231,74 @@ template <> struct OutStore<float> {
     static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *x) {
         __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, r, off, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])}, r, off + 16, 0, 0);
+    }
+};
+
+
+// Four consecutive io values starting at element i (i a multiple of 4), raw and
+// converted; the 4-wide counterparts of Vec8 / BufLoad8 / OutStore.
+template <typename IO> struct Vec4;
+template <> struct Vec4<uint16_t> {
+    struct Raw { uint2 u; };
+    static __device__ __forceinline__ Raw raw(const void *p, size_t i) {
+        return Raw{*reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i)};
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *x) {
+        x[0] = __uint_as_float(r.u.x << 16);
+        x[1] = __uint_as_float(r.u.x & 0xffff0000u);
+        x[2] = __uint_as_float(r.u.y << 16);
+        x[3] = __uint_as_float(r.u.y & 0xffff0000u);
+    }
+    static __device__ __forceinline__ uint2 pack(const float *x) {
+        return make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x[0], x[1]}, bf16x2_t)),
+                          __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x[2], x[3]}, bf16x2_t)));
+    }
+};
+template <> struct Vec4<float> {
+    struct Raw { float4 a; };
+    static __device__ __forceinline__ Raw raw(const void *p, size_t i) {
+        return Raw{*reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i)};
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *x) {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+    }
+};
+__device__ __forceinline__ void load4f(const float *p, float *x) {
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void store4f(float *p, const float *x) {
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+template <typename IO> struct BufLoad4;
+template <> struct BufLoad4<uint16_t> {
+    using Raw = typename Vec4<uint16_t>::Raw;
+    static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+        return Raw{make_uint2(v[0], v[1])};
+    }
+};
+template <> struct BufLoad4<float> {
+    using Raw = typename Vec4<float>::Raw;
+    static __device__ __forceinline__ Raw load(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+        return Raw{make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]))};
+    }
+};
+
+template <typename OUT> struct OutStore4;
+template <> struct OutStore4<uint16_t> {
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *x) {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const uint2 w = Vec4<uint16_t>::pack(x);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{w.x, w.y}, r, off, 0, 0);
+    }
+};
+template <> struct OutStore4<float> {
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *x) {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, r, off, 0, 0);
     }
 };
 

@@ -24,12 +24,14 @@
 // K3 puts under it") a 16-token chunk keeps e^{-G} <= e^80, inside the fp32 /
 // bf16 exponent range.
 //
-// Work layout: one workgroup of 4 waves per (sequence, head), walking the
-// sequence's chunks; about 64 KB of LDS, so two workgroups share a CU and
-// hide each other's latencies.  Wave w owns value columns 32w .. 32w+31 of S
-// and keeps that 128 x 32 fp32 slice in registers, in the accumulator layout
-// of the 16x16 MFMAs (lane l holds rows 16t + 4(l/16) + i, column l%16 of
-// each 16-column tile).  Contractions over the 16 tokens of a chunk
+// Work layout: one workgroup of 8 waves per (sequence, head), walking the
+// sequence's chunks; about 80 KB of LDS and at most 128 VGPRs, so two
+// workgroups share a CU (four waves per SIMD) and hide each other's
+// latencies.  Wave w owns value columns 16w .. 16w+15 of S and keeps that
+// 128 x 16 fp32 slice in registers, in the accumulator layout of the 16x16
+// MFMAs (lane l holds rows 16t + 4(l/16) + i, column l%16).  Element-wise
+// work maps thread x to token x/32 and four adjacent channels 4(x%32) ..
+// 4(x%32)+3.  Contractions over the 16 tokens of a chunk
 // (v_mfma_f32_16x16x16_bf16) take accumulator tiles directly as their B
 // operand.  Contractions over the 128 key channels (v_mfma_f32_16x16x32_bf16)
 // read S from the same registers: K slot 8h + i of a 32-channel step holds
@@ -47,46 +49,51 @@ namespace {
 
 using namespace chunk;
 
-constexpr int NW = 4;          // waves per workgroup
+constexpr int NW = 8;          // waves per workgroup
 constexpr int THREADS = NW * 64;
 
 
 // ------------------------------------------------------------------ LDS map (bytes)
 
-constexpr int OFF_KL = 0;                          // k^ Gamma (= Kbar), channel-permuted      hi,lo
-constexpr int OFF_QL = OFF_KL + 2 * PL_CD * 2;     // q^ Gamma (= Qbar), channel-permuted      hi,lo
-constexpr int OFF_KRD = OFF_QL + 2 * PL_CD * 2;    // k^ / Gamma, channel-permuted             hi,lo
-constexpr int OFF_O = OFF_KRD;                     // fp32 [16][132] output staging (after the Gram)
-constexpr int OFF_KHT = OFF_KRD + 2 * PL_CD * 2;   // Khat^T [channel][token], swizzled        hi,lo
-constexpr int OFF_V = OFF_KHT + 2 * PL_DC * 2;     // fp32 [16][132]
-constexpr int OFF_LA = OFF_V + C * FPK * 4;        // log alpha -> cumulative, fp32 [16][128]
-constexpr int OFF_AF = OFF_LA + C * D * 4;         // A (beta-scaled) fp32 [16][17]
-constexpr int OFF_PM = OFF_AF + C * 17 * 4;        // P                                        hi,lo [16][20]
-constexpr int OFF_TM = OFF_PM + 2 * PL_CC * 2;     // T                                        hi,lo [16][20]
-constexpr int OFF_BETA = OFF_TM + 2 * PL_CC * 2;   // fp32 [16]
-constexpr int OFF_EGC = OFF_BETA + C * 4;          // e^{G_C} fp32 [128]
-constexpr int OFF_CW = OFF_EGC + D * 4;            // conv weights fp32 [3 streams][4 taps][128]
-constexpr int OFF_RW = OFF_CW + 3 * 4 * D * 4;     // rms gain fp32 [128]
-constexpr int OFF_RAW = OFF_RW + D * 4;           // raw q, k, v rows of the chunk [3][16][128] io
-// ... then the last three raw rows of the previous chunks, double-buffered [2][3][3][128] io
-template <typename IO> struct RawLds {
-    static constexpr int CUR = OFF_RAW;
-    static constexpr int HIST = CUR + 3 * C * D * static_cast<int>(sizeof(IO));
-    static constexpr int BYTES = HIST + 2 * 3 * CONV_HIST * D * static_cast<int>(sizeof(IO));
-};
+// Pre-conv q, k, v rows staged as fp32, row-major [token][stream][128] for token
+// positions -3 .. 15 of the chunk: the three history rows come first, so the four
+// taps of a token are four fixed offsets from one address.  The history rows persist
+// from chunk to chunk; the chunk's own rows are dead once the convolution has read
+// them, and share their bytes with the K / Q / Khat operand planes written after it.
+constexpr int RAW_ROW = 3 * D * 4;                   // one token position, three streams
+constexpr int OFF_HIST = 0;                          // positions -3 .. -1
+constexpr int OFF_CUR = OFF_HIST + CONV_HIST * RAW_ROW;  // positions 0 .. 15
+constexpr int OFF_KL = OFF_CUR;                      // k^ Gamma (= Kbar), channel-permuted      hi,lo
+constexpr int OFF_QL = OFF_KL + 2 * PL_CD * 2;       // q^ Gamma (= Qbar), channel-permuted      hi,lo
+constexpr int OFF_KHT = OFF_QL + 2 * PL_CD * 2;      // Khat^T [channel][token], swizzled        hi,lo
+constexpr int OFF_KRD = OFF_KHT + 2 * PL_DC * 2;     // k^ / Gamma, channel-permuted             hi,lo
+constexpr int OFF_O = OFF_KRD;                       // fp32 [16][132] output staging (after the Gram)
+constexpr int OFF_V = OFF_KRD + 2 * PL_CD * 2;       // fp32 [16][132]
+constexpr int OFF_LA = OFF_V + C * FPK * 4;          // log2(alpha) -> cumulative, fp32 [16][128]
+constexpr int OFF_AF = OFF_LA + C * D * 4;           // A (beta-scaled) fp32 [16][17]
+constexpr int OFF_PM = OFF_AF + C * 17 * 4;          // P                                        hi,lo [16][20]
+constexpr int OFF_TM = OFF_PM + 2 * PL_CC * 2;       // T                                        hi,lo [16][20]
+constexpr int OFF_BETA = OFF_TM + 2 * PL_CC * 2;     // fp32 [16]
+constexpr int OFF_EGC = OFF_BETA + C * 4;            // e^{G_C} fp32 [128]
+constexpr int OFF_CW = OFF_EGC + D * 4;              // conv weights fp32 [3 streams][4 taps][128]
+constexpr int OFF_RW = OFF_CW + 3 * 4 * D * 4;       // rms gain fp32 [128]
+constexpr int LDS_BYTES = OFF_RW + D * 4;
 
+static_assert(C * RAW_ROW <= OFF_KRD - OFF_CUR, "staged rows must fit under the K / Q / Khat planes");
 static_assert(C * FPK * 4 <= 2 * PL_CD * 2, "output staging must fit in the KRD slot");
-static_assert(2 * RawLds<uint16_t>::BYTES <= 160 * 1024, "two bf16-io workgroups per gfx950 CU");
-static_assert(RawLds<float>::BYTES <= 160 * 1024, "one fp32-io workgroup per gfx950 CU");
+static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per gfx950 CU");
 
+constexpr float LOG2E = 1.4426950408889634f;
+
+// The second bound is waves per SIMD: two workgroups of 8 waves per CU need four
+// (at most 128 VGPRs).
 template <typename IO, typename OUT>
-__global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_kernel(LayerParams p) {
-    using IV = Vec8<IO>;
-    using IB = BufLoad8<IO>;
-    using OV = Vec8<OUT>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[RawLds<IO>::BYTES];
-    IO *const RAWC = reinterpret_cast<IO *>(smem + RawLds<IO>::CUR);
-    IO *const RAWH = reinterpret_cast<IO *>(smem + RawLds<IO>::HIST);
+__global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
+    using IV = Vec8<IO>;   // eight-wide rows of the conv cache
+    using I4 = Vec4<IO>;
+    using IB = BufLoad4<IO>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+    float *const RAW = reinterpret_cast<float *>(smem + OFF_HIST);  // [3 + 16][3][128]
     uint16_t *const KLh = reinterpret_cast<uint16_t *>(smem + OFF_KL);
     uint16_t *const QLh = reinterpret_cast<uint16_t *>(smem + OFF_QL);
     uint16_t *const KRDh = reinterpret_cast<uint16_t *>(smem + OFF_KRD);
@@ -117,43 +124,46 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_k
     const int lane = tid & 63;
     const int ln = lane & 15;        // MFMA row / column index
     const int lh = lane >> 4;        // MFMA K group
-    const int et = tid >> 4;         // element-wise token (0..15)
-    const int ec0 = (tid & 15) * 8;  // element-wise first channel
-    const int col0 = wave * 32 + ln; // value column of N-tile 0 (tile 1: +16)
+    const int et = tid >> 5;         // element-wise token (0..15)
+    const int ec0 = (tid & 31) * 4;  // element-wise first channel
+    const int col = wave * 16 + ln;  // value column of this lane's accumulator tiles
 
     // ---- per-head constants -----------------------------------------------------------
+    // The q and k weights are stored times log2(e): the convolution then yields
+    // z = log2(e) x, so that sigma(x) = 1 / (1 + 2^-z) needs no further scaling, and
+    // SiLU(x) log2(e) = z sigma(x), a constant factor that the L2 normalisation removes
+    // (its epsilon is scaled by log2(e)^2 to match).
     if (p.prologue) {
         for (int i = tid; i < 3 * D; i += THREADS) {
             const int s = i / D, c = i % D;
             const float4 w = *reinterpret_cast<const float4 *>(p.conv_w + ((s * HD) + hD + c) * 4);
-            CW[(s * 4 + 0) * D + c] = w.x;
-            CW[(s * 4 + 1) * D + c] = w.y;
-            CW[(s * 4 + 2) * D + c] = w.z;
-            CW[(s * 4 + 3) * D + c] = w.w;
+            const float f = s < 2 ? LOG2E : 1.0f;
+            CW[(s * 4 + 0) * D + c] = w.x * f;
+            CW[(s * 4 + 1) * D + c] = w.y * f;
+            CW[(s * 4 + 2) * D + c] = w.z * f;
+            CW[(s * 4 + 3) * D + c] = w.w * f;
         }
     }
     if (tid < D) RW[tid] = p.rms_w ? p.rms_w[tid] : 1.0f;
+    const float l2_eps = p.l2_eps * (LOG2E * LOG2E);
 
-    // ---- state slice in accumulator layout: S[t][nt][i] = S(16t + 4lh + i, col0 + 16nt) ----
+    // ---- state slice in accumulator layout: S[t][i] = S(16t + 4lh + i, col) ----------------
     const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D;
-    f32x4_t S[8][2];
+    f32x4_t S[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[t][nt][i] = p.state_in ? p.state_in[sbase + static_cast<size_t>(16 * t + 4 * lh + i) * D + col0 + 16 * nt] : 0.0f;
+        for (int i = 0; i < 4; ++i)
+            S[t][i] = p.state_in ? p.state_in[sbase + static_cast<size_t>(16 * t + 4 * lh + i) * D + col] : 0.0f;
 
     const int nchunks = (L + C - 1) / C;
-    const void *srcs[3] = {p.q, p.k, p.v};
 
     // Current-row loads of a chunk (q, k, v, log alpha, beta): issued one chunk ahead,
     // during the previous chunk's state products, so that their latency is hidden.
-    typename IV::Raw cur[3];
-    typename Vec8<float>::Raw lar;
+    typename I4::Raw cur[3];
+    typename Vec4<float>::Raw lar;
     float bet = 0.0f;
-    typename IV::Raw graw;
+    typename I4::Raw graw;
     // byte addresses of this (sequence, head)'s first row in each token-major tensor; a
     // chunk's rows start C rows further per chunk, and offsets inside a chunk fit 32 bits
     const uint32_t rowb_io = static_cast<uint32_t>(HD * sizeof(IO));
@@ -166,23 +176,29 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_k
     const char *beta_base = reinterpret_cast<const char *>(p.beta + static_cast<size_t>(t0) * H + h);
     const char *g_base = p.epilogue ? static_cast<const char *>(p.g) + first * sizeof(IO) : nullptr;
     char *o_base = static_cast<char *>(p.o) + first * sizeof(OUT);
-    const uint32_t off_io = static_cast<uint32_t>(et) * rowb_io + ec0 * sizeof(IO);
-    const uint32_t off_f = static_cast<uint32_t>(et) * rowb_f + ec0 * 4u;
 
+    // Per-thread offsets of the prefetches are rebuilt from an opaque copy of the thread
+    // index at each use rather than kept live across the loop: a spilled offset would
+    // be reloaded with a wait that also drains the prefetches in flight.
     auto load_current = [&](int c) {
+        const int x = opaque(tid), xt = x >> 5, xc = (x & 31) * 4;
         const int r0 = c * C, nrow = min(L, r0 + C) - r0;
         const size_t cio = static_cast<size_t>(r0) * rowb_io;
+        const uint32_t off_io = static_cast<uint32_t>(xt) * rowb_io + xc * sizeof(IO);
 #pragma unroll
         for (int s = 0; s < 3; ++s)
             cur[s] = IB::load(rows_view(qkv_base[s] + cio, nrow, rowb_io, D * sizeof(IO)), off_io);
-        lar = BufLoad8<float>::load(rows_view(la_base + static_cast<size_t>(r0) * rowb_f, nrow, rowb_f, D * 4), off_f);
+        lar = BufLoad4<float>::load(rows_view(la_base + static_cast<size_t>(r0) * rowb_f, nrow, rowb_f, D * 4),
+                                    static_cast<uint32_t>(xt) * rowb_f + xc * 4u);
         bet = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            rows_view(beta_base + static_cast<size_t>(r0) * H * 4, nrow, H * 4, 4), static_cast<uint32_t>(et * H) * 4u, 0, 0));
+            rows_view(beta_base + static_cast<size_t>(r0) * H * 4, nrow, H * 4, 4), static_cast<uint32_t>(xt * H) * 4u, 0, 0));
     };
     auto load_gate = [&](int c) {
+        const int x = opaque(tid);
         const int r0 = c * C, nrow = min(L, r0 + C) - r0;
         if (p.epilogue)
-            graw = IB::load(rows_view(g_base + static_cast<size_t>(r0) * rowb_io, nrow, rowb_io, D * sizeof(IO)), off_io);
+            graw = IB::load(rows_view(g_base + static_cast<size_t>(r0) * rowb_io, nrow, rowb_io, D * sizeof(IO)),
+                            static_cast<uint32_t>(x >> 5) * rowb_io + (x & 31) * 4 * sizeof(IO));
     };
     if (nchunks > 0) {
         load_current(0);
@@ -191,10 +207,14 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_k
     if (p.prologue && tid < 3 * CONV_HIST * 16) {
         // history of the first chunk: the given conv cache (oldest first) or zeros
         const int s = tid / (CONV_HIST * 16), j = (tid / 16) % CONV_HIST, c0 = (tid & 15) * 8;
-        typename IV::Raw r{};
-        if (p.conv_in) r = IV::raw(p.conv_in, ((static_cast<size_t>(n) * 3 + s) * CONV_HIST + j) * HD + hD + c0);
-        *reinterpret_cast<typename IV::Raw *>(RAWH + ((1 * 3 + s) * CONV_HIST + j) * D + c0) = r;
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (p.conv_in) IV::load(p.conv_in, ((static_cast<size_t>(n) * 3 + s) * CONV_HIST + j) * HD + hD + c0, x);
+        store4f(RAW + (j * 3 + s) * D + c0, x);
+        store4f(RAW + (j * 3 + s) * D + c0 + 4, x + 4);
     }
+
+    // this thread's staged row (position et) and the same row three positions earlier
+    float *const raw_t = RAW + ((CONV_HIST + et) * 3) * D + ec0;
 
     for (int ch = 0; ch < nchunks; ++ch) {
         const int r0 = ch * C;                 // first position of the chunk
@@ -202,68 +222,74 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_k
         const int pos = r0 + et;               // this thread's token position
         const bool valid = pos < L;
 
-        // ---- 1. stage this chunk's raw rows (prefetched during the previous chunk) -------------
-        const int hb = ch & 1;  // history buffer written by this chunk (read by the next)
+        // ---- 1. stage this chunk's rows (prefetched during the previous chunk) as fp32 --------
+        float xr[3][4];  // this thread's pre-conv values: tap 0 of its convolution
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
-            *reinterpret_cast<typename IV::Raw *>(RAWC + (s * C + et) * D + ec0) = cur[s];
-            if (et >= C - CONV_HIST)
-                *reinterpret_cast<typename IV::Raw *>(RAWH + ((hb * 3 + s) * CONV_HIST + et - (C - CONV_HIST)) * D + ec0) = cur[s];
+            I4::unpack(cur[s], xr[s]);
+            store4f(raw_t + s * D, xr[s]);
         }
         {
-            float la[8];
-            Vec8<float>::unpack(lar, la);
-            Vec8<float>::store(LA, et * D + ec0, la);
-            if ((tid & 15) == 0) BETA[et] = bet;
+            float la[4];
+            Vec4<float>::unpack(lar, la);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) la[e] *= LOG2E;
+            store4f(LA + et * D + ec0, la);
+            if ((tid & 31) == 0) BETA[et] = bet;
         }
         __syncthreads();
 
         // ---- 2. conv4 + SiLU (+ L2 for q, k) from the staged rows; cumulative log-decay -------
-        float xq[8], xk[8], xv[8];
+        float xq[4], xk[4], xv[4];
         {
             float *outs[3] = {xq, xk, xv};
 #pragma unroll
             for (int s = 0; s < 3; ++s) {
                 float *a = outs[s];
-                IV::unpack(*reinterpret_cast<const typename IV::Raw *>(RAWC + (s * C + et) * D + ec0), a);
                 if (p.prologue) {
-                    float acc[8], w[8];
-                    Vec8<float>::load(CW, (s * 4) * D + ec0, w);
+                    float acc[4], w[4];
+                    load4f(CW + (s * 4) * D + ec0, w);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] = w[e] * a[e];
+                    for (int e = 0; e < 4; ++e) acc[e] = w[e] * xr[s][e];
 #pragma unroll
                     for (int j = 1; j <= 3; ++j) {
-                        const int r = et - j;  // row in this chunk, or (r + 3) in the history
-                        const IO *src = r >= 0 ? RAWC + (s * C + r) * D
-                                               : RAWH + (((hb ^ 1) * 3 + s) * CONV_HIST + r + CONV_HIST) * D;
-                        float xj[8];
-                        IV::unpack(*reinterpret_cast<const typename IV::Raw *>(src + ec0), xj);
-                        Vec8<float>::load(CW, (s * 4 + j) * D + ec0, w);
+                        float xj[4];
+                        load4f(raw_t + (s - 3 * j) * D, xj);
+                        load4f(CW + (s * 4 + j) * D + ec0, w);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[e], xj[e], acc[e]);
+                        for (int e = 0; e < 4; ++e) acc[e] = fmaf(w[e], xj[e], acc[e]);
                     }
+                    if (s < 2) {  // acc = log2(e) x:  z sigma(x) = z / (1 + 2^-z)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) a[e] = siluf_(acc[e]);
+                        for (int e = 0; e < 4; ++e)
+                            a[e] = acc[e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc[e]));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) a[e] = siluf_(acc[e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] = xr[s][e];
                 }
             }
             if (p.prologue) {
                 float sq = 0.f, sk = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
+                for (int e = 0; e < 4; ++e) {
                     sq = fmaf(xq[e], xq[e], sq);
                     sk = fmaf(xk[e], xk[e], sk);
                 }
-                sq = group_sum<16>(sq);
-                sk = group_sum<16>(sk);
-                const float iq = rsqrtf(sq + p.l2_eps), ik = rsqrtf(sk + p.l2_eps);
+                sq = half_wave_sum(sq);
+                sk = half_wave_sum(sk);
+                const float iq = __builtin_amdgcn_rsqf(sq + l2_eps), ik = __builtin_amdgcn_rsqf(sk + l2_eps);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
+                for (int e = 0; e < 4; ++e) {
                     xq[e] *= iq;
                     xk[e] *= ik;
                 }
                 if (!valid) {  // padding tokens past the end see real history rows: clear them
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) xq[e] = xk[e] = xv[e] = 0.0f;
+                    for (int e = 0; e < 4; ++e) xq[e] = xk[e] = xv[e] = 0.0f;
                 }
             }
         }
@@ -275,55 +301,56 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_k
                 g += LA[r * D + c];
                 LA[r * D + c] = g;
             }
-            EGC[c] = __expf(g);
+            EGC[c] = __builtin_amdgcn_exp2f(g);
         }
         __syncthreads();
 
-        // ---- 3. staged operands (bf16 hi/lo) ------------------------------------------------
-        {
-            float gl[8];
-            Vec8<float>::load(LA, et * D + ec0, gl);
-            float kl[8], ql[8], krd[8];
+        // ---- 3. staged operands (bf16 hi/lo); the next chunk's conv history ------------------
+        if (et >= C - CONV_HIST) {
+            // the last three positions become positions -3 .. -1 of the next chunk (the
+            // convolution has read the old ones: the barrier above orders it)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float E = __expf(gl[e]);
-                const float rE = __expf(-gl[e]);
+            for (int s = 0; s < 3; ++s) store4f(raw_t + (s - 3 * C) * D, xr[s]);
+        }
+        {
+            float gl[4], egc[4];
+            load4f(LA + et * D + ec0, gl);
+            load4f(EGC + ec0, egc);
+            float kl[4], ql[4], krd[4], kht[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float E = __builtin_amdgcn_exp2f(gl[e]);
+                const float rE = __builtin_amdgcn_exp2f(-gl[e]);
                 kl[e] = xk[e] * E;
                 ql[e] = xq[e] * E;
                 krd[e] = xk[e] * rE;
+                kht[e] = krd[e] * egc[e];
             }
-            // channel-permuted positions of channels ec0..ec0+3 and ec0+4..ec0+7
-            const int pc0 = cperm(ec0), pc1 = cperm(ec0 + 4);
-            const int rp = et * OPK;
-            uint4 hi, lo;
-            split8(kl, hi, lo);
-            *reinterpret_cast<uint2 *>(KLh + rp + pc0) = make_uint2(hi.x, hi.y);
-            *reinterpret_cast<uint2 *>(KLh + rp + pc1) = make_uint2(hi.z, hi.w);
-            *reinterpret_cast<uint2 *>(KLh + PL_CD + rp + pc0) = make_uint2(lo.x, lo.y);
-            *reinterpret_cast<uint2 *>(KLh + PL_CD + rp + pc1) = make_uint2(lo.z, lo.w);
-            split8(ql, hi, lo);
-            *reinterpret_cast<uint2 *>(QLh + rp + pc0) = make_uint2(hi.x, hi.y);
-            *reinterpret_cast<uint2 *>(QLh + rp + pc1) = make_uint2(hi.z, hi.w);
-            *reinterpret_cast<uint2 *>(QLh + PL_CD + rp + pc0) = make_uint2(lo.x, lo.y);
-            *reinterpret_cast<uint2 *>(QLh + PL_CD + rp + pc1) = make_uint2(lo.z, lo.w);
-            split8(krd, hi, lo);
-            *reinterpret_cast<uint2 *>(KRDh + rp + pc0) = make_uint2(hi.x, hi.y);
-            *reinterpret_cast<uint2 *>(KRDh + rp + pc1) = make_uint2(hi.z, hi.w);
-            *reinterpret_cast<uint2 *>(KRDh + PL_CD + rp + pc0) = make_uint2(lo.x, lo.y);
-            *reinterpret_cast<uint2 *>(KRDh + PL_CD + rp + pc1) = make_uint2(lo.z, lo.w);
+            // channels ec0 .. ec0+3 keep their order at channel-permuted position cperm(ec0)
+            const int at = et * OPK + cperm(ec0);
+            uint2 hi, lo;
+            split4(kl, hi, lo);
+            *reinterpret_cast<uint2 *>(KLh + at) = hi;
+            *reinterpret_cast<uint2 *>(KLh + PL_CD + at) = lo;
+            split4(ql, hi, lo);
+            *reinterpret_cast<uint2 *>(QLh + at) = hi;
+            *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = lo;
+            split4(krd, hi, lo);
+            *reinterpret_cast<uint2 *>(KRDh + at) = hi;
+            *reinterpret_cast<uint2 *>(KRDh + PL_CD + at) = lo;
             // Khat^T[c][t] = k^_t[c] e^{G_C[c] - G_t[c]}
+            split4(kht, hi, lo);
+            const uint32_t hw[4] = {hi.x, hi.x >> 16, hi.y, hi.y >> 16};
+            const uint32_t lw[4] = {lo.x, lo.x >> 16, lo.y, lo.y >> 16};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < 4; ++e) {
                 const int c = ec0 + e;
-                uint16_t sh, sl;
-                split1(krd[e] * EGC[c], sh, sl);
-                KHTh[c * OPT + kht_col(c, et)] = sh;
-                KHTh[PL_DC + c * OPT + kht_col(c, et)] = sl;
+                KHTh[c * OPT + kht_col(c, et)] = static_cast<uint16_t>(hw[e]);
+                KHTh[PL_DC + c * OPT + kht_col(c, et)] = static_cast<uint16_t>(lw[e]);
             }
-            Vec8<float>::store(VB, et * FPK + ec0, xv);
+            store4f(VB + et * FPK + ec0, xv);
         }
         __syncthreads();
-
         // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
         if (wave < 2) {
             const uint16_t *Lh = wave == 0 ? KLh : QLh;
@@ -337,8 +364,8 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_k
                 const uint4 bl = *reinterpret_cast<const uint4 *>(KRDh + PL_CD + ka);
                 acc = mma3(ah, al, bh, bl, acc);
             }
-            const int j = ln;
             if (wave == 0) {
+                const int x = opaque(lane), ln = x & 15, lh = x >> 4, j = ln;
                 // T = (I + A)^{-1} Diag(beta).  With B = -A (strictly lower, so B^16 = 0),
                 // (I + A)^{-1} = sum_{k<16} B^k = (I + B)(I + B^2)(I + B^4)(I + B^8):
                 // four levels of 16x16 products on the matrix cores.  Every matrix M is
@@ -385,6 +412,7 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_k
                 *reinterpret_cast<uint2 *>(TMh + ln * OPT + 4 * lh) = th;
                 *reinterpret_cast<uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh) = tl;
             } else {
+                const int j = ln;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 4 * lh + i;
@@ -397,12 +425,7 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_k
         }
         // X = V - Kbar S0 and O1 = Qbar S0.  S0 is the B operand: K step s holds rows
         // 32s + pi(slot), split into bf16 hi/lo right before use.
-        f32x4_t X[2], O1[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            X[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            O1[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        f32x4_t X = {0.f, 0.f, 0.f, 0.f}, O1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int ka = ln * OPK + 32 * s + 8 * lh;
@@ -410,86 +433,67 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_k
             const uint4 kl_ = *reinterpret_cast<const uint4 *>(KLh + PL_CD + ka);
             const uint4 qh = *reinterpret_cast<const uint4 *>(QLh + ka);
             const uint4 ql_ = *reinterpret_cast<const uint4 *>(QLh + PL_CD + ka);
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const float v8[8] = {S[2 * s][nt][0], S[2 * s][nt][1], S[2 * s][nt][2], S[2 * s][nt][3],
-                                     S[2 * s + 1][nt][0], S[2 * s + 1][nt][1], S[2 * s + 1][nt][2], S[2 * s + 1][nt][3]};
-                uint4 sh, sl;
-                split8(v8, sh, sl);
-                X[nt] = mma3(kh, kl_, sh, sl, X[nt]);
-                O1[nt] = mma3(qh, ql_, sh, sl, O1[nt]);
-            }
+            const float v8[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
+                                 S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
+            uint4 sh, sl;
+            split8(v8, sh, sl);
+            X = mma3(kh, kl_, sh, sl, X);
+            O1 = mma3(qh, ql_, sh, sl, O1);
         }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X[nt][i] = VB[(4 * lh + i) * FPK + col0 + 16 * nt] - X[nt][i];
+        for (int i = 0; i < 4; ++i) X[i] = VB[(4 * lh + i) * FPK + col] - X[i];
         __syncthreads();
 
         // ---- 5. U = T X, O = scale (Qbar S + P U), S <- Diag(Gamma_C) S + Khat^T U -------------
         if (ch + 1 < nchunks) load_current(ch + 1);
         {
-            uint2 Th, Tl, Ph, Pl;
-            Th = *reinterpret_cast<const uint2 *>(TMh + ln * OPT + 4 * lh);
-            Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh);
-            Ph = *reinterpret_cast<const uint2 *>(PMh + ln * OPT + 4 * lh);
-            Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + ln * OPT + 4 * lh);
-            uint2 Uh[2], Ul[2];
+            const uint2 Th = *reinterpret_cast<const uint2 *>(TMh + ln * OPT + 4 * lh);
+            const uint2 Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh);
+            const uint2 Ph = *reinterpret_cast<const uint2 *>(PMh + ln * OPT + 4 * lh);
+            const uint2 Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + ln * OPT + 4 * lh);
+            const Split4 Xs(X);
+            const Split4 Us(mma16_3(Th, Tl, Xs.h, Xs.l, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+            // P U goes to its own accumulator: a K = 16 MFMA accumulating onto the result of
+            // a K = 32 MFMA read stale accumulator rows on gfx950 (observed, not documented),
+            // so the two chains never share an accumulator and are summed on the VALU.
+            const f32x4_t O2 = mma16_3(Ph, Pl, Us.h, Us.l, f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                uint2 xh, xl;
-                const float x4[4] = {X[nt][0], X[nt][1], X[nt][2], X[nt][3]};
-                split4(x4, xh, xl);
-                const f32x4_t U = mma16_3(Th, Tl, xh, xl, f32x4_t{0.f, 0.f, 0.f, 0.f});
-                const float u4[4] = {U[0], U[1], U[2], U[3]};
-                split4(u4, Uh[nt], Ul[nt]);
-            }
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                // P U goes to its own accumulator: a K = 16 MFMA accumulating onto the result of
-                // a K = 32 MFMA read stale accumulator rows on gfx950 (observed, not documented),
-                // so the two chains never share an accumulator and are summed on the VALU.
-                const f32x4_t O2 = mma16_3(Ph, Pl, Uh[nt], Ul[nt], f32x4_t{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col0 + 16 * nt] = (O1[nt][i] + O2[i]) * p.scale;
-            }
+            for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = (O1[i] + O2[i]) * p.scale;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int c = 16 * t + ln;
                 const int ka = c * OPT + kht_col(c, 4 * lh);
                 const uint2 ah = *reinterpret_cast<const uint2 *>(KHTh + ka);
                 const uint2 al = *reinterpret_cast<const uint2 *>(KHTh + PL_DC + ka);
-                float g4[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) g4[i] = EGC[16 * t + 4 * lh + i];
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) S[t][nt][i] *= g4[i];
-                    S[t][nt] = mma16_3(ah, al, Uh[nt], Ul[nt], S[t][nt]);
-                }
+                const float4 g4 = *reinterpret_cast<const float4 *>(EGC + 16 * t + 4 * lh);
+                S[t][0] *= g4.x;
+                S[t][1] *= g4.y;
+                S[t][2] *= g4.z;
+                S[t][3] *= g4.w;
+                S[t] = mma16_3(ah, al, Us.h, Us.l, S[t]);
             }
         }
         __syncthreads();
 
         // ---- 6. epilogue: sigma(g) * RMSNorm(o~) * w ------------------------------------------
         {
-            float o[8];
-            Vec8<float>::load(OB, et * FPK + ec0, o);
+            float o[4];
+            load4f(OB + et * FPK + ec0, o);
             if (p.epilogue) {
                 float ss = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ss = fmaf(o[e], o[e], ss);
-                ss = group_sum<16>(ss);
-                const float inv = rsqrtf(ss * (1.0f / D) + p.rms_eps);
-                float g[8];
-                IV::unpack(graw, g);
+                for (int e = 0; e < 4; ++e) ss = fmaf(o[e], o[e], ss);
+                ss = half_wave_sum(ss);
+                const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.rms_eps);
+                float g[4], rw[4];
+                I4::unpack(graw, g);
+                load4f(RW + ec0, rw);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = sigmoidf_(g[e]) * (o[e] * inv) * RW[ec0 + e];
+                for (int e = 0; e < 4; ++e) o[e] = sigmoidf_(g[e]) * (o[e] * inv) * rw[e];
             }
-            OutStore<OUT>::store(rows_view(o_base + static_cast<size_t>(r0) * HD * sizeof(OUT), rend - r0,
-                                           static_cast<uint32_t>(HD * sizeof(OUT)), D * sizeof(OUT)),
-                                 static_cast<uint32_t>(et) * static_cast<uint32_t>(HD * sizeof(OUT)) + ec0 * sizeof(OUT), o);
+            OutStore4<OUT>::store(rows_view(o_base + static_cast<size_t>(r0) * HD * sizeof(OUT), rend - r0,
+                                            static_cast<uint32_t>(HD * sizeof(OUT)), D * sizeof(OUT)),
+                                  static_cast<uint32_t>(et) * static_cast<uint32_t>(HD * sizeof(OUT)) + ec0 * sizeof(OUT), o);
         }
         if (ch + 1 < nchunks) load_gate(ch + 1);
         // the next chunk's first two barriers order these LDS reads before any rewrite
@@ -497,13 +501,12 @@ __global__ __launch_bounds__(THREADS, sizeof(IO) == 2 ? 2 : 1) void chunked_tp_k
 
     // ---- final state and conv cache ------------------------------------------------------
     if (p.state_out) {
+        const int x = opaque(tid);  // addresses built here, not kept live through the loop
+        float *const so = p.state_out + sbase + static_cast<size_t>(4 * ((x & 63) >> 4)) * D + (x >> 6) * 16 + (x & 15);
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    p.state_out[sbase + static_cast<size_t>(16 * t + 4 * lh + i) * D + col0 + 16 * nt] = S[t][nt][i];
+            for (int i = 0; i < 4; ++i) so[(16 * t + i) * D] = S[t][i];
     }
     if (p.prologue && p.conv_out) {
         // the last three pre-conv inputs of each stream, oldest first; rows before the

@@ -97,6 +97,19 @@ __device__ __forceinline__ f32x4_t mma(uint4 a, uint4 b, f32x4_t c) {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// (a_hi + a_lo)(b_hi + b_lo) without the lo*lo term for a K = 16 contraction held in
+// K = 16 operand layouts (lane group g: K indices 4g .. 4g+3), as two K = 32 MFMAs (the
+// same issue cost as one K = 16 MFMA on gfx950).  Slots 0-3 of a lane carry the hi parts
+// of its four K indices and slots 4-7 the lo parts: (a_hi, a_lo) against (b_hi, b_hi),
+// then against (b_lo, 0).  Accumulating a K = 16 MFMA onto a K = 32 result read stale
+// accumulator rows on gfx950 (observed, not documented), so the kernels never mix the
+// two shapes on one accumulator.
+__device__ __forceinline__ f32x4_t mma16x2(uint2 ahi, uint2 alo, uint2 bhi, uint2 blo, f32x4_t c) {
+    const uint4 a = make_uint4(ahi.x, ahi.y, alo.x, alo.y);
+    c = mma(a, make_uint4(bhi.x, bhi.y, bhi.x, bhi.y), c);
+    return mma(a, make_uint4(blo.x, blo.y, 0u, 0u), c);
+}
+
 // (a_hi + a_lo)(b_hi + b_lo) without the lo*lo term.
 __device__ __forceinline__ f32x4_t mma3(uint4 ahi, uint4 alo, uint4 bhi, uint4 blo, f32x4_t c) {
     c = mma(alo, bhi, c);
@@ -117,7 +130,7 @@ __device__ __forceinline__ int opaque(int x) {
 // and one ds_swizzle that exchanges the two 16-lane rows of the half.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float half_wave_sum(float x) {
     x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]: lane ^ 1

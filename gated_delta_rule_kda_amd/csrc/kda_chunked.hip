@@ -55,6 +55,16 @@ constexpr int THREADS = NW * 64;
 
 // ------------------------------------------------------------------ LDS map (bytes)
 
+// Khat^T plane: row c holds the 16 hi parts of the chunk's tokens, then the 16 lo parts,
+// then 4 padding elements (KHTR = 36 bf16), so one 16-byte pair of reads fetches both
+// parts of a 4-token group.  Token t sits at t XOR 2 ((c / 16) % 8) inside each part:
+// every aligned group of four tokens stays contiguous (the MFMA operand reads; odd
+// c / 16 swaps the group's two halves), and both the transposing 16-bit stores (32
+// lanes: 32 channels 4 apart, one token) and the operand reads (16 lanes: 16
+// consecutive channels) hit 32 distinct banks.
+constexpr int KHTR = 2 * C + 4;
+__device__ __forceinline__ int kht_pos(int c, int t) { return c * KHTR + (t ^ (2 * ((c >> 4) & 7))); }
+
 // Pre-conv q, k, v rows staged as fp32, row-major [token][stream][128] for token
 // positions -3 .. 15 of the chunk: the three history rows come first, so the four
 // taps of a token are four fixed offsets from one address.  The history rows persist
@@ -65,13 +75,14 @@ constexpr int OFF_HIST = 0;                          // positions -3 .. -1
 constexpr int OFF_CUR = OFF_HIST + CONV_HIST * RAW_ROW;  // positions 0 .. 15
 constexpr int OFF_KL = OFF_CUR;                      // k^ Gamma (= Kbar), channel-permuted      hi,lo
 constexpr int OFF_QL = OFF_KL + 2 * PL_CD * 2;       // q^ Gamma (= Qbar), channel-permuted      hi,lo
-constexpr int OFF_KHT = OFF_QL + 2 * PL_CD * 2;      // Khat^T [channel][token], swizzled        hi,lo
-constexpr int OFF_KRD = OFF_KHT + 2 * PL_DC * 2;     // k^ / Gamma, channel-permuted             hi,lo
+constexpr int OFF_KHT = OFF_QL + 2 * PL_CD * 2;      // Khat^T [channel][hi 16 | lo 16 | pad]   swizzled
+constexpr int OFF_KRD = OFF_KHT + D * KHTR * 2;      // k^ / Gamma, channel-permuted             hi,lo
 constexpr int OFF_O = OFF_KRD;                       // fp32 [16][132] output staging (after the Gram)
 constexpr int OFF_V = OFF_KRD + 2 * PL_CD * 2;       // fp32 [16][132]
 constexpr int OFF_LA = OFF_V + C * FPK * 4;          // log2(alpha) -> cumulative, fp32 [16][128]
-constexpr int OFF_AF = OFF_LA + C * D * 4;           // A (beta-scaled) fp32 [16][17]
-constexpr int OFF_PM = OFF_AF + C * 17 * 4;          // P                                        hi,lo [16][20]
+constexpr int AFK = 20;                              // row of the A staging (k-major)
+constexpr int OFF_AF = OFF_LA + C * D * 4;           // A (beta-scaled) fp32 [16][4][4], rows of AFK
+constexpr int OFF_PM = OFF_AF + C * AFK * 4;         // P                                        hi,lo [16][20]
 constexpr int OFF_TM = OFF_PM + 2 * PL_CC * 2;       // T                                        hi,lo [16][20]
 constexpr int OFF_BETA = OFF_TM + 2 * PL_CC * 2;     // fp32 [16]
 constexpr int OFF_EGC = OFF_BETA + C * 4;            // e^{G_C} fp32 [128]
@@ -84,6 +95,7 @@ static_assert(C * FPK * 4 <= 2 * PL_CD * 2, "output staging must fit in the KRD 
 static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per gfx950 CU");
 
 constexpr float LOG2E = 1.4426950408889634f;
+
 
 // The second bound is waves per SIMD: two workgroups of 8 waves per CU need four
 // (at most 128 VGPRs).
@@ -345,14 +357,17 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = ec0 + e;
-                KHTh[c * OPT + kht_col(c, et)] = static_cast<uint16_t>(hw[e]);
-                KHTh[PL_DC + c * OPT + kht_col(c, et)] = static_cast<uint16_t>(lw[e]);
+                KHTh[kht_pos(c, et)] = static_cast<uint16_t>(hw[e]);
+                KHTh[C + kht_pos(c, et)] = static_cast<uint16_t>(lw[e]);
             }
             store4f(VB + et * FPK + ec0, xv);
         }
         __syncthreads();
         // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
         if (wave < 2) {
+            // the Gram blocks and T gate the next barrier for the whole workgroup: their
+            // waves take issue priority over the other waves of their SIMDs meanwhile
+            __builtin_amdgcn_s_setprio(2);
             const uint16_t *Lh = wave == 0 ? KLh : QLh;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -365,52 +380,47 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 acc = mma3(ah, al, bh, bl, acc);
             }
             if (wave == 0) {
-                const int x = opaque(lane), ln = x & 15, lh = x >> 4, j = ln;
-                // T = (I + A)^{-1} Diag(beta).  With B = -A (strictly lower, so B^16 = 0),
-                // (I + A)^{-1} = sum_{k<16} B^k = (I + B)(I + B^2)(I + B^4)(I + B^8):
-                // four levels of 16x16 products on the matrix cores.  Every matrix M is
-                // kept in two register forms: "b" = B-operand / accumulator layout (lane
-                // (n, g) holds M[4g+i][n]) and "a" = A-operand layout (lane (m, g) holds
-                // M[m][4g+i]); the product XY takes (a of X, b of Y) and gives b of XY,
-                // while (b of Y, a of X) gives b of (XY)^T = a of XY.
-                float bb[4], ba[4];
+                // T = (I + A)^{-1} Diag(beta) by forward substitution in fp32: lane 4j + r
+                // carries rows r, r+4, r+8, r+12 of column j of (I + A)^{-1}; step k
+                // broadcasts row k inside the quad and removes A[i][k] x_k from every row
+                // (A is strictly lower, so rows i <= k are left unchanged).  A goes through
+                // LDS k-major, AF[k][r][q] = A[4q + r][k], so that step k reads one float4.
+                {
+                    const float4 b4 = *reinterpret_cast<const float4 *>(BETA + 4 * lh);
+                    const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * lh + i;
-                    bb[i] = j < r ? -acc[i] * BETA[r] : 0.0f;
-                    AF[r * 17 + j] = bb[i];
+                    for (int i = 0; i < 4; ++i) AF[ln * AFK + 4 * i + lh] = ln < 4 * lh + i ? acc[i] * bv[i] : 0.0f;
                 }
-                // one transpose through LDS for the a form of B
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                const int x = opaque(lane), j = x >> 2, r = x & 3;
+                float xv[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ba[i] = AF[ln * 17 + 4 * lh + i];
-                // Only the a form of the sum is needed (T is an A operand).  Each operand is
-                // split into bf16 hi/lo once and reused by the products that read it.
-                float sa[4];  // a form of S1 = I + B
+                for (int q = 0; q < 4; ++q) xv[q] = (4 * q + r == j) ? 1.0f : 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sa[i] = ba[i] + ((4 * lh + i) == ln ? 1.0f : 0.0f);
-                Split4 Ba(ba), Bb(bb);
-                Split4 B2b(mm16s(Ba, Bb)), B2a(mm16s(Bb, Ba));           // B^2
-                float t[4];
-                mm16s(B2b, Split4(sa), t);                                 // S2 = S1 + S1 B^2
+                for (int k = 0; k < C; ++k) {
+                    float xk;
+                    switch (k & 3) {  // x_k, from lane 4j + k % 4 of the quad
+                        case 0: xk = dpp<0x00>(xv[k >> 2]); break;
+                        case 1: xk = dpp<0x55>(xv[k >> 2]); break;
+                        case 2: xk = dpp<0xAA>(xv[k >> 2]); break;
+                        default: xk = dpp<0xFF>(xv[k >> 2]); break;
+                    }
+                    const float4 a = *reinterpret_cast<const float4 *>(AF + k * AFK + 4 * r);
+                    xv[0] = fmaf(-a.x, xk, xv[0]);
+                    xv[1] = fmaf(-a.y, xk, xv[1]);
+                    xv[2] = fmaf(-a.z, xk, xv[2]);
+                    xv[3] = fmaf(-a.w, xk, xv[3]);
+                }
+                const float bj = BETA[j];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sa[i] += t[i];
-                Split4 B4b(mm16s(B2a, B2b)), B4a(mm16s(B2b, B2a));       // B^4
-                mm16s(B4b, Split4(sa), t);                                 // S4 = S2 + S2 B^4
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sa[i] += t[i];
-                Split4 B8b(mm16s(B4a, B4b));                               // B^8
-                mm16s(B8b, Split4(sa), t);                                 // S8 = S4 + S4 B^8
-                // T[m][k] = S8[m][k] beta_k: lane (m, g) stores row m, columns 4g .. 4g+3
-                float tv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) tv[i] = (sa[i] + t[i]) * BETA[4 * lh + i];
-                uint2 th, tl;
-                split4(tv, th, tl);
-                *reinterpret_cast<uint2 *>(TMh + ln * OPT + 4 * lh) = th;
-                *reinterpret_cast<uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh) = tl;
+                for (int q = 0; q < 4; ++q) {
+                    uint16_t sh, sl;
+                    split1(xv[q] * bj, sh, sl);
+                    TMh[(4 * q + r) * OPT + j] = sh;
+                    TMh[PL_CC + (4 * q + r) * OPT + j] = sl;
+                }
             } else {
                 const int j = ln;
 #pragma unroll
@@ -422,6 +432,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     PMh[PL_CC + r * OPT + j] = sl;
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         // X = V - Kbar S0 and O1 = Qbar S0.  S0 is the B operand: K step s holds rows
         // 32s + pi(slot), split into bf16 hi/lo right before use.
@@ -452,25 +463,30 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             const uint2 Ph = *reinterpret_cast<const uint2 *>(PMh + ln * OPT + 4 * lh);
             const uint2 Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + ln * OPT + 4 * lh);
             const Split4 Xs(X);
-            const Split4 Us(mma16_3(Th, Tl, Xs.h, Xs.l, f32x4_t{0.f, 0.f, 0.f, 0.f}));
-            // P U goes to its own accumulator: a K = 16 MFMA accumulating onto the result of
-            // a K = 32 MFMA read stale accumulator rows on gfx950 (observed, not documented),
-            // so the two chains never share an accumulator and are summed on the VALU.
-            const f32x4_t O2 = mma16_3(Ph, Pl, Us.h, Us.l, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            const Split4 Us(mma16x2(Th, Tl, Xs.h, Xs.l, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+            const f32x4_t O = mma16x2(Ph, Pl, Us.h, Us.l, O1);  // Qbar S + P U
 #pragma unroll
-            for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = (O1[i] + O2[i]) * p.scale;
+            for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = O[i] * p.scale;
+            // Khat^T U with the products split as in mma16x2.  Rows of odd tiles hold their
+            // two token pairs swapped (the plane's bank swizzle), so those tiles take the
+            // U operand with its pairs swapped to match.
+            const uint4 ub_e = make_uint4(Us.h.x, Us.h.y, Us.h.x, Us.h.y), ul_e = make_uint4(Us.l.x, Us.l.y, 0u, 0u);
+            const uint4 ub_o = make_uint4(Us.h.y, Us.h.x, Us.h.y, Us.h.x), ul_o = make_uint4(Us.l.y, Us.l.x, 0u, 0u);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int c = 16 * t + ln;
-                const int ka = c * OPT + kht_col(c, 4 * lh);
+                // tokens 4lh .. 4lh+3 of row c sit at group lh ^ (t / 2)
+                const int ka = c * KHTR + 4 * (lh ^ (t >> 1));
                 const uint2 ah = *reinterpret_cast<const uint2 *>(KHTh + ka);
-                const uint2 al = *reinterpret_cast<const uint2 *>(KHTh + PL_DC + ka);
+                const uint2 al = *reinterpret_cast<const uint2 *>(KHTh + C + ka);
+                const uint4 a = make_uint4(ah.x, ah.y, al.x, al.y);
                 const float4 g4 = *reinterpret_cast<const float4 *>(EGC + 16 * t + 4 * lh);
                 S[t][0] *= g4.x;
                 S[t][1] *= g4.y;
                 S[t][2] *= g4.z;
                 S[t][3] *= g4.w;
-                S[t] = mma16_3(ah, al, Us.h, Us.l, S[t]);
+                S[t] = mma(a, (t & 1) ? ub_o : ub_e, S[t]);
+                S[t] = mma(a, (t & 1) ? ul_o : ul_e, S[t]);
             }
         }
         __syncthreads();

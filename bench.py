@@ -70,7 +70,8 @@ def cpu_info() -> str:
 
 
 KERNEL_SOURCES = {
-    "prefill": ["gated_delta_rule_kda_amd/csrc/kda_chunked.hip", "gated_delta_rule_kda_amd/csrc/kda_internal.h"],
+    "prefill": ["gated_delta_rule_kda_amd/csrc/kda_chunked.hip", "gated_delta_rule_kda_amd/csrc/kda_chunk_common.h",
+                "gated_delta_rule_kda_amd/csrc/kda_internal.h"],
     "decode": ["gated_delta_rule_kda_amd/csrc/kda_recurrent.hip", "gated_delta_rule_kda_amd/csrc/kda_internal.h"],
 }
 

@@ -101,7 +101,7 @@ def load_traffic(path: str) -> dict:
     return out
 
 
-def run_extra_workloads(kda, W, dev, stream, log) -> dict:
+def run_extra_workloads(kda, W, dev, stream, log, algo="auto") -> dict:
     """Time the long-context (1 x 131072) and packed variable-length (64 sequences)
     prefills: inputs generated one sequence at a time straight into device buffers."""
     import torch
@@ -131,7 +131,7 @@ def run_extra_workloads(kda, W, dev, stream, log) -> dict:
         log(f"{name}: generated {T} tokens in {time.perf_counter() - t0:.1f}s")
         cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
         cwd = torch.from_numpy(cw).to(dev)
-        cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", prologue=True, epilogue=True)
+        cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", prologue=True, epilogue=True, algo=algo)
         o = torch.empty((T, H, D), dtype=bf, device=dev)
         s_out = torch.empty_like(s0)
         ws_n = kda.workspace_size(cfg, N, T)
@@ -308,7 +308,7 @@ def main() -> int:
         log(f"oracle: {L0} tokens x {H} heads in {ct:.1f}s on {threads} threads")
 
     traffic = load_traffic(args.traffic)
-    extra = run_extra_workloads(kda, W, dev, stream, log) if args.extra_workloads else None
+    extra = run_extra_workloads(kda, W, dev, stream, log, args.algo) if args.extra_workloads else None
 
     res = {
         "metric": "KDA prefill tokens/sec (H=96,d=128) + decode state GB/s at B=256",

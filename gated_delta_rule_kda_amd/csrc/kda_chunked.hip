@@ -280,8 +280,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                         for (int e = 0; e < 4; ++e) a[e] = siluf_(acc[e]);
                     }
                 } else {
+                    const float f = s == 0 ? p.scale : 1.0f;  // q carries the read scale
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) a[e] = xr[s][e];
+                    for (int e = 0; e < 4; ++e) a[e] = xr[s][e] * f;
                 }
             }
             if (p.prologue) {
@@ -293,7 +294,8 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 }
                 sq = half_wave_sum(sq);
                 sk = half_wave_sum(sk);
-                const float iq = __builtin_amdgcn_rsqf(sq + l2_eps), ik = __builtin_amdgcn_rsqf(sk + l2_eps);
+                // q also carries the read scale (O = scale (Qbar S + P U) is linear in q)
+                const float iq = __builtin_amdgcn_rsqf(sq + l2_eps) * p.scale, ik = __builtin_amdgcn_rsqf(sk + l2_eps);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     xq[e] *= iq;
@@ -369,7 +371,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             // waves take issue priority over the other waves of their SIMDs meanwhile
             __builtin_amdgcn_s_setprio(2);
             const uint16_t *Lh = wave == 0 ? KLh : QLh;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            // two independent accumulation chains (channels 0-63 and 64-127) halve the
+            // dependent-MFMA latency on this critical path
+            f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int s = 0; s < D / 32; ++s) {
                 const int ka = ln * OPK + 32 * s + 8 * lh;
@@ -377,8 +381,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 const uint4 al = *reinterpret_cast<const uint4 *>(Lh + PL_CD + ka);
                 const uint4 bh = *reinterpret_cast<const uint4 *>(KRDh + ka);
                 const uint4 bl = *reinterpret_cast<const uint4 *>(KRDh + PL_CD + ka);
-                acc = mma3(ah, al, bh, bl, acc);
+                acc2[s >> 1] = mma3(ah, al, bh, bl, acc2[s >> 1]);
             }
+            const f32x4_t acc = acc2[0] + acc2[1];
             if (wave == 0) {
                 // T = (I + A)^{-1} Diag(beta) by forward substitution in fp32: lane 4j + r
                 // carries rows r, r+4, r+8, r+12 of column j of (I + A)^{-1}; step k
@@ -453,6 +458,21 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[i] = VB[(4 * lh + i) * FPK + col] - X[i];
+        const Split4 Xs(X);
+        // S has been read: decay it now, S <- Diag(Gamma_C) S, in the time the Gram / T
+        // waves need before the barrier (they decay theirs after it)
+        const bool late_decay = wave == 0;
+        auto decay = [&]() {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float4 g4 = *reinterpret_cast<const float4 *>(EGC + 16 * t + 4 * lh);
+                S[t][0] *= g4.x;
+                S[t][1] *= g4.y;
+                S[t][2] *= g4.z;
+                S[t][3] *= g4.w;
+            }
+        };
+        if (!late_decay) decay();
         __syncthreads();
 
         // ---- 5. U = T X, O = scale (Qbar S + P U), S <- Diag(Gamma_C) S + Khat^T U -------------
@@ -462,11 +482,11 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             const uint2 Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh);
             const uint2 Ph = *reinterpret_cast<const uint2 *>(PMh + ln * OPT + 4 * lh);
             const uint2 Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + ln * OPT + 4 * lh);
-            const Split4 Xs(X);
             const Split4 Us(mma16x2(Th, Tl, Xs.h, Xs.l, f32x4_t{0.f, 0.f, 0.f, 0.f}));
             const f32x4_t O = mma16x2(Ph, Pl, Us.h, Us.l, O1);  // Qbar S + P U
 #pragma unroll
-            for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = O[i] * p.scale;
+            for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = O[i];
+            if (late_decay) decay();
             // Khat^T U with the products split as in mma16x2.  Rows of odd tiles hold their
             // two token pairs swapped (the plane's bank swizzle), so those tiles take the
             // U operand with its pairs swapped to match.
@@ -480,11 +500,6 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 const uint2 ah = *reinterpret_cast<const uint2 *>(KHTh + ka);
                 const uint2 al = *reinterpret_cast<const uint2 *>(KHTh + C + ka);
                 const uint4 a = make_uint4(ah.x, ah.y, al.x, al.y);
-                const float4 g4 = *reinterpret_cast<const float4 *>(EGC + 16 * t + 4 * lh);
-                S[t][0] *= g4.x;
-                S[t][1] *= g4.y;
-                S[t][2] *= g4.z;
-                S[t][3] *= g4.w;
                 S[t] = mma(a, (t & 1) ? ub_o : ub_e, S[t]);
                 S[t] = mma(a, (t & 1) ? ul_o : ul_e, S[t]);
             }

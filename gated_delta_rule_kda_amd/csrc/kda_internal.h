@@ -36,7 +36,6 @@ struct LayerParams {
 hipError_t launch_recurrent(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s);
 hipError_t launch_chunked_throughput(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s);
 hipError_t launch_chunked_latency(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s);
-int device_cu_count();  // compute units of the current device (cached per device)
 hipError_t launch_order(const int32_t *cu_seqlens, int32_t n, int32_t *order, hipStream_t s);
 size_t order_workspace_bytes(int32_t n);
 

@@ -68,15 +68,16 @@ typedef int32_t kda_status;
 #define KDA_DTYPE_BF16 1
 
 /* Prefill algorithm.  AUTO picks CHUNKED for bf16 inputs and RECURRENT for fp32.
- * CHUNKED picks one of its two variants from the launch shape: THROUGHPUT when
- * there are more (sequence, head) items than compute units, LATENCY otherwise.
- * All chunked variants compute in 16-token chunks on the matrix cores with
- * bf16 hi/lo operand splits and fp32 accumulation (about 1e-4 relative to an
- * fp64 evaluation); RECURRENT is the fp32 reference-precision path. */
+ * CHUNKED resolves to the THROUGHPUT variant, the faster one on every launch shape
+ * measured (4 x 4096, 1 x 131072 and 64 packed sequences, 96 heads); the LATENCY
+ * variant stays selectable by name.  All chunked variants compute in 16-token
+ * chunks on the matrix cores with bf16 hi/lo operand splits and fp32
+ * accumulation (about 1e-4 relative to an fp64 evaluation); RECURRENT is the
+ * fp32 reference-precision path. */
 #define KDA_ALGO_AUTO 0
 #define KDA_ALGO_RECURRENT 1            /* token-sequential fp32 recurrence */
-#define KDA_ALGO_CHUNKED 2              /* chunked, variant chosen from the launch shape */
-#define KDA_ALGO_CHUNKED_THROUGHPUT 3   /* two 4-wave workgroups per compute unit */
+#define KDA_ALGO_CHUNKED 2              /* chunked, the variant the library prefers */
+#define KDA_ALGO_CHUNKED_THROUGHPUT 3   /* 8-wave workgroups, two per compute unit */
 #define KDA_ALGO_CHUNKED_LATENCY 4      /* one 8-wave producer/consumer workgroup per compute unit */
 
 typedef struct {
@@ -130,8 +131,8 @@ kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
 kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *args, void *hip_stream);
 
 /* The KDA_ALGO_* that kda_prefill runs for this configuration and num_seqs
- * sequences on the current device (AUTO and CHUNKED resolved), or -1 when the
- * configuration is invalid or num_seqs <= 0.  Host only; enqueues nothing. */
+ * sequences (AUTO and CHUNKED resolved), or -1 when the configuration is
+ * invalid or num_seqs <= 0.  Host only; enqueues nothing. */
 int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs);
 
 /* -------------------------------------------------------------- decode step

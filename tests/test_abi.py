@@ -142,7 +142,8 @@ def test_resolved_algo():
     assert kda.resolved_algo(c, 3) == "recurrent"
     for name in ("recurrent", "chunked_throughput", "chunked_latency"):
         assert kda.resolved_algo(kda.config(4, algo=name), 2) == name
-    assert kda.resolved_algo(kda.config(8), 1) in ("chunked_throughput", "chunked_latency")
+    assert kda.resolved_algo(kda.config(8), 1) == "chunked_throughput"
+    assert kda.resolved_algo(kda.config(96, algo="chunked"), 4) == "chunked_throughput"
     assert L.kda_prefill_resolved_algo(ctypes.byref(kda.config(4)), 0) == -1
     bad = kda.config(4)
     bad.algo = 9

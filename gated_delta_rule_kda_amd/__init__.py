@@ -53,13 +53,14 @@ class PrefillArgs(ctypes.Structure):
                 ("q", _vp), ("k", _vp), ("v", _vp), ("log_alpha", _vp), ("beta", _vp), ("g", _vp),
                 ("conv_w", _vp), ("conv_in", _vp), ("conv_out", _vp), ("rms_w", _vp),
                 ("state_in", _vp), ("state_out", _vp), ("o", _vp), ("workspace", _vp),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("state_in_slots", _vp), ("state_out_slots", _vp)]
 
 
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("q", _vp), ("k", _vp), ("v", _vp),
                 ("log_alpha", _vp), ("beta", _vp), ("g", _vp), ("conv_w", _vp),
-                ("conv_state", _vp), ("rms_w", _vp), ("state", _vp), ("slots", _vp), ("o", _vp)]
+                ("conv_state", _vp), ("rms_w", _vp), ("state", _vp), ("slots", _vp), ("o", _vp),
+                ("slots_out", _vp)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -159,10 +160,14 @@ def workspace_size(cfg: Config, num_seqs: int, total_tokens: int) -> int:
 
 def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_in=None,
             conv_out=None, rms_w=None, state_in=None, state_out=None, o=None, workspace=None,
+            state_in_slots=None, state_out_slots=None,
             cfg: Optional[Config] = None, return_state: bool = True, return_conv: bool = True,
             stream=None, **cfg_kwargs) -> Tuple[object, object, object]:
     """kda_prefill on torch tensors.  q, k, v, g: [T, H, 128]; log_alpha [T, H, 128] fp32;
     beta [T, H] fp32; cu_seqlens int32 [N+1] on the device.  Missing outputs are allocated.
+    With state_in_slots / state_out_slots (int32 [N] on the device) the state and conv arrays
+    are pools of rows [rows, H, 128, 128] / [rows, 3, 3, H*128] and sequence n reads row
+    state_in_slots[n] and writes row state_out_slots[n]; outputs are then not allocated.
     Returns (o, state_out, conv_out)."""
     import torch
     T, H = q.shape[0], q.shape[1]
@@ -183,19 +188,25 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     _expect(beta, "beta", torch.float32, (T, H))
     _expect(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
     _expect(conv_w, "conv_w", torch.float32, (3, H * D, 4))
-    _expect(conv_in, "conv_in", io_t, (N, 3, 3, H * D))
+    _expect(state_in_slots, "state_in_slots", torch.int32, (N,))
+    _expect(state_out_slots, "state_out_slots", torch.int32, (N,))
+    rows_in = N if state_in_slots is None else (None if state_in is None else state_in.shape[0])
+    rows_ci = N if state_in_slots is None else (None if conv_in is None else conv_in.shape[0])
+    rows_out = N if state_out_slots is None else (None if state_out is None else state_out.shape[0])
+    rows_co = N if state_out_slots is None else (None if conv_out is None else conv_out.shape[0])
+    _expect(conv_in, "conv_in", io_t, (rows_ci, 3, 3, H * D))
     _expect(rms_w, "rms_w", torch.float32, (D,))
-    _expect(state_in, "state_in", torch.float32, (N, H, D, D))
+    _expect(state_in, "state_in", torch.float32, (rows_in, H, D, D))
     dev = q.device
     if o is None:
         o = torch.empty((T, H, D), dtype=out_t, device=dev)
     _expect(o, "o", out_t, (T, H, D))
-    if state_out is None and return_state:
+    if state_out is None and return_state and state_out_slots is None:
         state_out = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
-    _expect(state_out, "state_out", torch.float32, (N, H, D, D))
-    if conv_out is None and return_conv and cfg.prologue:
+    _expect(state_out, "state_out", torch.float32, (rows_out, H, D, D))
+    if conv_out is None and return_conv and cfg.prologue and state_out_slots is None:
         conv_out = torch.empty((N, 3, 3, H * D), dtype=io_t, device=dev)
-    _expect(conv_out, "conv_out", io_t, (N, 3, 3, H * D))
+    _expect(conv_out, "conv_out", io_t, (rows_co, 3, 3, H * D))
     need = workspace_size(cfg, N, T)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -207,16 +218,18 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     a.state_in, a.state_out, a.o = _ptr(state_in), _ptr(state_out), _ptr(o)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.state_in_slots, a.state_out_slots = _ptr(state_in_slots), _ptr(state_out_slots)
     _check(lib().kda_prefill(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
     return o, state_out, conv_out
 
 
 def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_state=None,
-                rms_w=None, slots=None, o=None, cfg: Optional[Config] = None, stream=None,
-                **cfg_kwargs):
+                rms_w=None, slots=None, slots_out=None, o=None, cfg: Optional[Config] = None,
+                stream=None, **cfg_kwargs):
     """kda_decode_step on torch tensors: one token per request, q, k, v, g [B, H, 128];
-    state [slots, H, 128, 128] and conv_state [slots, 3, 3, H*128] are updated in place.
-    Returns o [B, H, 128]."""
+    state [rows, H, 128, 128] and conv_state [rows, 3, 3, H*128] are pools updated in place:
+    request b reads row slots[b] (b when None) and writes row slots_out[b] (its read row
+    when None).  Returns o [B, H, 128]."""
     import torch
     B, H, D = q.shape
     if cfg is None:
@@ -241,6 +254,9 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
         _expect(conv_state, "conv_state", io_t, (conv_state.shape[0], 3, 3, H * D))
     _expect(rms_w, "rms_w", torch.float32, (D,))
     _expect(slots, "slots", torch.int32, (B,))
+    _expect(slots_out, "slots_out", torch.int32, (B,))
+    if slots_out is not None and slots is None and n_slots < B:
+        raise ValueError("state has fewer rows than requests")
     if o is None:
         o = torch.empty((B, H, D), dtype=out_t, device=q.device)
     _expect(o, "o", out_t, (B, H, D))
@@ -250,6 +266,7 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
                                                _ptr(beta), _ptr(g))
     a.conv_w, a.conv_state, a.rms_w = _ptr(conv_w), _ptr(conv_state), _ptr(rms_w)
     a.state, a.slots, a.o = _ptr(state), _ptr(slots), _ptr(o)
+    a.slots_out = _ptr(slots_out)
     _check(lib().kda_decode_step(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
     return o
 

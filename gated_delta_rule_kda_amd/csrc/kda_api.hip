@@ -131,7 +131,8 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
         !ok_ptr(a->o, tok) || !ok_ptr(a->g, tok && cfg->epilogue) ||
         !ok_ptr(a->conv_w, cfg->prologue != 0) || !ok_ptr(a->conv_in, false) ||
         !ok_ptr(a->conv_out, false) || !ok_ptr(a->rms_w, false) || !ok_ptr(a->state_in, false) ||
-        !ok_ptr(a->state_out, false) || !ok_ptr(a->workspace, false))
+        !ok_ptr(a->state_out, false) || !ok_ptr(a->workspace, false) ||
+        !ok_ptr(a->state_in_slots, false) || !ok_ptr(a->state_out_slots, false))
         return KDA_ERR_INVALID_ARGUMENT;
     const size_t need = order_workspace_bytes(a->num_seqs);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
@@ -156,6 +157,7 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     p.conv_in = cfg->prologue ? a->conv_in : nullptr;
     p.conv_out = cfg->prologue ? a->conv_out : nullptr;
     p.state_in = a->state_in; p.state_out = a->state_out; p.o = a->o;
+    p.slots_in = a->state_in_slots; p.slots_out = a->state_out_slots;
     p.scale = cfg->scale; p.l2_eps = cfg->l2_eps; p.rms_eps = cfg->rms_eps;
     p.prologue = cfg->prologue; p.epilogue = cfg->epilogue;
     if (trace_enabled())
@@ -181,13 +183,14 @@ kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *a, void
         !ok_ptr(a->log_alpha, true) || !ok_ptr(a->beta, true) || !ok_ptr(a->o, true) ||
         !ok_ptr(a->state, true) || !ok_ptr(a->g, cfg->epilogue != 0) ||
         !ok_ptr(a->conv_w, cfg->prologue != 0) || !ok_ptr(a->conv_state, cfg->prologue != 0) ||
-        !ok_ptr(a->rms_w, false) || !ok_ptr(a->slots, false))
+        !ok_ptr(a->rms_w, false) || !ok_ptr(a->slots, false) || !ok_ptr(a->slots_out, false))
         return KDA_ERR_INVALID_ARGUMENT;
     LayerParams p{};
     p.H = cfg->num_heads;
     p.num_items = a->batch * cfg->num_heads;
     p.cu_seqlens = nullptr;
-    p.slots = a->slots;
+    p.slots_in = a->slots;
+    p.slots_out = a->slots_out ? a->slots_out : a->slots;
     p.q = a->q; p.k = a->k; p.v = a->v; p.g = cfg->epilogue ? a->g : nullptr;
     p.log_alpha = a->log_alpha; p.beta = a->beta;
     p.conv_w = cfg->prologue ? a->conv_w : nullptr;

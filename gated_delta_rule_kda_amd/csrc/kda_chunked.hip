@@ -160,7 +160,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     const float l2_eps = p.l2_eps * (LOG2E * LOG2E);
 
     // ---- state slice in accumulator layout: S[t][i] = S(16t + 4lh + i, col) ----------------
-    const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D;
+    const int row_in = p.slots_in ? p.slots_in[n] : n;     // state_in / conv_in row
+    const int row_out = p.slots_out ? p.slots_out[n] : n;  // state_out / conv_out row
+    const size_t sbase = (static_cast<size_t>(row_in) * H + h) * D * D;
     f32x4_t S[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         // history of the first chunk: the given conv cache (oldest first) or zeros
         const int s = tid / (CONV_HIST * 16), j = (tid / 16) % CONV_HIST, c0 = (tid & 15) * 8;
         float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (p.conv_in) IV::load(p.conv_in, ((static_cast<size_t>(n) * 3 + s) * CONV_HIST + j) * HD + hD + c0, x);
+        if (p.conv_in) IV::load(p.conv_in, ((static_cast<size_t>(row_in) * 3 + s) * CONV_HIST + j) * HD + hD + c0, x);
         store4f(RAW + (j * 3 + s) * D + c0, x);
         store4f(RAW + (j * 3 + s) * D + c0 + 4, x + 4);
     }
@@ -533,7 +535,8 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     // ---- final state and conv cache ------------------------------------------------------
     if (p.state_out) {
         const int x = opaque(tid);  // addresses built here, not kept live through the loop
-        float *const so = p.state_out + sbase + static_cast<size_t>(4 * ((x & 63) >> 4)) * D + (x >> 6) * 16 + (x & 15);
+        float *const so = p.state_out + (static_cast<size_t>(row_out) * H + h) * D * D +
+                          static_cast<size_t>(4 * ((x & 63) >> 4)) * D + (x >> 6) * 16 + (x & 15);
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -554,11 +557,11 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             if (pj >= 0)
                 IV::load(srcs[s], static_cast<size_t>(t0 + pj) * HD + hD + cg * 8, x);
             else if (p.conv_in)
-                IV::load(p.conv_in, ((static_cast<size_t>(n) * 3 + s) * CONV_HIST + (CONV_HIST + pj)) * HD + hD + cg * 8, x);
+                IV::load(p.conv_in, ((static_cast<size_t>(row_in) * 3 + s) * CONV_HIST + (CONV_HIST + pj)) * HD + hD + cg * 8, x);
         }
         __syncthreads();
         if (active)
-            IV::store(p.conv_out, ((static_cast<size_t>(n) * 3 + s) * CONV_HIST + j) * HD + hD + cg * 8, x);
+            IV::store(p.conv_out, ((static_cast<size_t>(row_out) * 3 + s) * CONV_HIST + j) * HD + hD + cg * 8, x);
     }
 }
 

@@ -149,7 +149,10 @@ __global__ __launch_bounds__(THREADS, 1) void chunked_pipe_kernel(LayerParams p)
     const size_t first = static_cast<size_t>(t0) * HD + hD;
     const uint32_t off_io = static_cast<uint32_t>(et) * rowb_io + ec0 * sizeof(IO);
     const uint32_t off_f = static_cast<uint32_t>(et) * rowb_f + ec0 * 4u;
-    const size_t sbase = (static_cast<size_t>(n) * H + h) * D * D;
+    const int row_in = p.slots_in ? p.slots_in[n] : n;     // state_in / conv_in row
+    const int row_out = p.slots_out ? p.slots_out[n] : n;  // state_out / conv_out row
+    const size_t sbase = (static_cast<size_t>(row_in) * H + h) * D * D;
+    const size_t sbase_out = (static_cast<size_t>(row_out) * H + h) * D * D;
 
     // ---- role state ----------------------------------------------------------------------
     // consumer: the state slice S[t][nt][i] = S(16t + 4lh + i, col0 + 16nt), and the gate
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(THREADS, 1) void chunked_pipe_kernel(LayerParams p)
             // history of the first chunk: the given conv cache (oldest first) or zeros
             const int s = gt / (CONV_HIST * 16), j = (gt / 16) % CONV_HIST, c0 = (gt & 15) * 8;
             typename IV::Raw r{};
-            if (p.conv_in) r = IV::raw(p.conv_in, ((static_cast<size_t>(n) * 3 + s) * CONV_HIST + j) * HD + hD + c0);
+            if (p.conv_in) r = IV::raw(p.conv_in, ((static_cast<size_t>(row_in) * 3 + s) * CONV_HIST + j) * HD + hD + c0);
             *reinterpret_cast<typename IV::Raw *>(RAWH + ((1 * 3 + s) * CONV_HIST + j) * D + c0) = r;
         }
     }
@@ -529,7 +532,7 @@ __global__ __launch_bounds__(THREADS, 1) void chunked_pipe_kernel(LayerParams p)
             for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    p.state_out[sbase + static_cast<size_t>(16 * t + 4 * lh + i) * D + col0 + 16 * nt] = S[t][nt][i];
+                    p.state_out[sbase_out + static_cast<size_t>(16 * t + 4 * lh + i) * D + col0 + 16 * nt] = S[t][nt][i];
     }
     if (p.prologue && p.conv_out) {
         // the last three pre-conv inputs of each stream, oldest first; rows before the
@@ -546,11 +549,11 @@ __global__ __launch_bounds__(THREADS, 1) void chunked_pipe_kernel(LayerParams p)
             if (pj >= 0)
                 IV::load(srcs[s], static_cast<size_t>(t0 + pj) * HD + hD + cg * 8, x);
             else if (p.conv_in)
-                IV::load(p.conv_in, ((static_cast<size_t>(n) * 3 + s) * CONV_HIST + (CONV_HIST + pj)) * HD + hD + cg * 8, x);
+                IV::load(p.conv_in, ((static_cast<size_t>(row_in) * 3 + s) * CONV_HIST + (CONV_HIST + pj)) * HD + hD + cg * 8, x);
         }
         __syncthreads();
         if (active)
-            IV::store(p.conv_out, ((static_cast<size_t>(n) * 3 + s) * CONV_HIST + j) * HD + hD + cg * 8, x);
+            IV::store(p.conv_out, ((static_cast<size_t>(row_out) * 3 + s) * CONV_HIST + j) * HD + hD + cg * 8, x);
     }
 }
 

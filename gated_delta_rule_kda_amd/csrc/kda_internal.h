@@ -18,7 +18,8 @@ struct LayerParams {
     int32_t H;
     int32_t num_items;           // work items = sequences (or requests) x heads
     const int32_t *cu_seqlens;   // prefill: [N+1]; decode: NULL (one token per request)
-    const int32_t *slots;        // decode: state / conv row of each request (NULL = identity)
+    const int32_t *slots_in;     // row of state_in / conv_in of each sequence or request (NULL = identity)
+    const int32_t *slots_out;    // row of state_out / conv_out of each sequence or request (NULL = identity)
     const int32_t *order;        // prefill: longest-first sequence order (NULL = identity)
     const void *q, *k, *v, *g;
     const float *log_alpha, *beta;

@@ -48,17 +48,18 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
     const int idx = item / H;
 
     int64_t t0, t1;
-    int srow;  // row of state / conv cache
+    int n;  // sequence (prefill) or request (decode)
     if (p.cu_seqlens) {
-        const int n = p.order ? p.order[idx] : idx;
+        n = p.order ? p.order[idx] : idx;
         t0 = p.cu_seqlens[n];
         t1 = p.cu_seqlens[n + 1];
-        srow = n;
     } else {
+        n = idx;
         t0 = idx;
         t1 = idx + 1;
-        srow = p.slots ? p.slots[idx] : idx;
     }
+    const int row_in = p.slots_in ? p.slots_in[n] : n;     // state_in / conv_in row
+    const int row_out = p.slots_out ? p.slots_out[n] : n;  // state_out / conv_out row
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
     __shared__ float sh_beta[2];
 
     // ---- state in registers -------------------------------------------------
-    const size_t sbase = (static_cast<size_t>(srow) * H + h) * D * D;
+    const size_t sbase = (static_cast<size_t>(row_in) * H + h) * D * D;
     float S[16][4];
     if (p.state_in) {
         const float4 *src = reinterpret_cast<const float4 *>(p.state_in + sbase);
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
             wB[j] = qk_lane ? wb[j] : 0.f;
         }
         if (p.conv_in) {
-            const size_t base = static_cast<size_t>(srow) * 3 * CONV_HIST * HD + h * D + c;
+            const size_t base = static_cast<size_t>(row_in) * 3 * CONV_HIST * HD + h * D + c;
 #pragma unroll
             for (int j = 0; j < CONV_HIST; ++j) {
                 hA[j] = IOT::load(p.conv_in, base + (sA * CONV_HIST + j) * HD);
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
 
     // ---- final state and conv cache ----------------------------------------------
     if (p.state_out) {
-        float4 *dst = reinterpret_cast<float4 *>(p.state_out + sbase);
+        float4 *dst = reinterpret_cast<float4 *>(p.state_out + (static_cast<size_t>(row_out) * H + h) * D * D);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const f32x4v y = {S[r][0], S[r][1], S[r][2], S[r][3]};
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
         }
     }
     if (p.prologue && p.conv_out) {
-        const size_t base = static_cast<size_t>(srow) * 3 * CONV_HIST * HD + h * D + c;
+        const size_t base = static_cast<size_t>(row_out) * 3 * CONV_HIST * HD + h * D + c;
 #pragma unroll
         for (int j = 0; j < CONV_HIST; ++j) {
             IOT::store(p.conv_out, base + (sA * CONV_HIST + j) * HD, hA[j]);

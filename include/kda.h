@@ -53,7 +53,7 @@ extern "C" {
 #endif
 
 #define KDA_HEAD_DIM 128
-#define KDA_ABI_VERSION 1u
+#define KDA_ABI_VERSION 2u
 
 /* Status codes. */
 typedef int32_t kda_status;
@@ -100,9 +100,18 @@ void kda_config_init(kda_config *cfg, int32_t num_heads);
 /* ------------------------------------------------------------------ prefill
  * Runs the whole layer core over N packed variable-length sequences.
  * Sequence n covers tokens [cu_seqlens[n], cu_seqlens[n+1]); it starts from
- * state_in[n] (zeros when NULL) and conv_in[n] (zeros when NULL) and leaves
- * its final state in state_out[n] and its last three pre-conv inputs in
- * conv_out[n].  A zero-length sequence copies state and cache through.
+ * state_in[r_in] (zeros when NULL) and conv_in[r_in] (zeros when NULL) and
+ * leaves its final state in state_out[r_out] and its last three pre-conv
+ * inputs in conv_out[r_out].  The rows are r_in = state_in_slots[n] and
+ * r_out = state_out_slots[n], or n where a slot array is NULL, so the state
+ * and conv arrays can be pools of per-request rows ("Kimi K3: Architecture and
+ * SGLang Day-0 Support", "SGLang's day-0 adaptations": per-request state that
+ * can be snapshotted and restored).  Reading a prefix checkpoint row and
+ * writing another row is a copy-on-write fork; a row written by one sequence
+ * must not be read or written by another sequence of the same call.
+ * A zero-length sequence copies state and cache from its in row to its out row.
+ * Speculative verification runs draft tokens from the committed rows with
+ * state_out and conv_out NULL, then replays the accepted tokens in place.
  */
 typedef struct {
     int32_t num_seqs;             /* N > 0 */
@@ -113,14 +122,16 @@ typedef struct {
     const float *beta;            /* [T][H] fp32, in [0, 1] */
     const void *g;                /* [T][H][128] io_dtype; required iff epilogue */
     const float *conv_w;          /* [3][H*128][4] fp32; required iff prologue */
-    const void *conv_in;          /* [N][3][3][H*128] io_dtype or NULL (zero history) */
+    const void *conv_in;          /* [rows][3][3][H*128] io_dtype or NULL (zero history) */
     void *conv_out;               /* same layout or NULL (not written); may alias conv_in */
     const float *rms_w;           /* [128] fp32 or NULL (ones) */
-    const float *state_in;        /* [N][H][128][128] fp32 or NULL (zeros) */
+    const float *state_in;        /* [rows][H][128][128] fp32 or NULL (zeros) */
     float *state_out;             /* same layout or NULL (not written); may alias state_in */
     void *o;                      /* [T][H][128] out_dtype; must not alias any input */
     void *workspace;              /* device scratch of at least kda_prefill_workspace_size bytes */
     size_t workspace_bytes;
+    const int32_t *state_in_slots;   /* device [N] rows of state_in / conv_in, or NULL (row n) */
+    const int32_t *state_out_slots;  /* device [N] rows of state_out / conv_out, or NULL (row n) */
 } kda_prefill_args;
 
 /* Bytes of device workspace kda_prefill needs for N sequences (it holds the
@@ -139,7 +150,11 @@ int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs);
  * One token per request, the same layer core as prefill at T = 1 per
  * sequence: the conv caches are shifted and the state is updated in place
  * ("Kimi K3: Architecture and SGLang Day-0 Support": each step reads and
- * writes only S, which is overwritten in place).
+ * writes only S, which is overwritten in place).  Request b reads pool row
+ * slots[b] and writes pool row slots_out[b] (the same row when slots_out is
+ * NULL); a distinct out row forks the request from a read-only checkpoint
+ * (copy on write).  A row written by one request must not be read or written
+ * by another request of the same call.
  */
 typedef struct {
     int32_t batch;                /* B > 0 requests */
@@ -151,8 +166,9 @@ typedef struct {
     void *conv_state;             /* [slots][3][3][H*128] io_dtype, updated in place; required iff prologue */
     const float *rms_w;           /* [128] fp32 or NULL (ones) */
     float *state;                 /* [slots][H][128][128] fp32, updated in place */
-    const int32_t *slots;         /* device [B] pool slot of each request, or NULL (slot b for request b) */
+    const int32_t *slots;         /* device [B] pool row each request reads, or NULL (row b) */
     void *o;                      /* [B][H][128] out_dtype */
+    const int32_t *slots_out;     /* device [B] pool row each request writes, or NULL (its slots row) */
 } kda_decode_args;
 
 kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *args, void *hip_stream);

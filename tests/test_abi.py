@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_sizes():
-    assert kda.abi_version() == 1
+    assert kda.abi_version() == 2
     assert kda.state_bytes(96) == 96 * 128 * 128 * 4
     # the pages' per-request figure: 69 KDA layers x 12 heads per GPU at TP=8 x 128^2 x fp32
     assert abs(69 * kda.state_bytes(12) / 1e6 - 54.26) < 0.01
@@ -85,6 +85,26 @@ def test_prefill_rejects_null_required(field):
 def test_prefill_rejects_misaligned():
     assert _prefill(kda.config(4), _args(q=FAKE + 2)) == kda.ERR_INVALID_ARGUMENT
     assert _prefill(kda.config(4), _args(state_in=FAKE + 8)) == kda.ERR_INVALID_ARGUMENT
+    assert _prefill(kda.config(4), _args(state_in_slots=FAKE + 4)) == kda.ERR_INVALID_ARGUMENT
+    assert _prefill(kda.config(4), _args(state_out_slots=FAKE + 4)) == kda.ERR_INVALID_ARGUMENT
+
+
+def _header_fields(struct_name):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^{}]*)\}\s*" + struct_name + ";", text).group(1)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if decl:
+            names += [re.sub(r"[^A-Za-z0-9_]", "", part.split()[-1]) for part in decl.split(",")]
+    return names
+
+
+@pytest.mark.parametrize("cname, ctype", [("kda_config", kda.Config), ("kda_prefill_args", kda.PrefillArgs),
+                                          ("kda_decode_args", kda.DecodeArgs)])
+def test_binding_structs_match_header(cname, ctype):
+    """The ctypes structures declare the header's fields in the header's order."""
+    assert [f for f, _ in ctype._fields_] == _header_fields(cname)
 
 
 def test_prefill_rejects_bad_config():
@@ -131,6 +151,7 @@ def test_decode_rejects_bad_arguments():
         assert dec(kda.config(4), **{f: None}) == kda.ERR_INVALID_ARGUMENT, f
     assert dec(kda.config(4), batch=0) == kda.ERR_INVALID_ARGUMENT
     assert dec(kda.config(4), slots=FAKE + 4) == kda.ERR_INVALID_ARGUMENT
+    assert dec(kda.config(4), slots_out=FAKE + 4) == kda.ERR_INVALID_ARGUMENT
     assert dec(kda.config(4, head_dim=256)) == kda.ERR_UNSUPPORTED
 
 

@@ -104,14 +104,16 @@ void kda_config_init(kda_config *cfg, int32_t num_heads);
  * leaves its final state in state_out[r_out] and its last three pre-conv
  * inputs in conv_out[r_out].  The rows are r_in = state_in_slots[n] and
  * r_out = state_out_slots[n], or n where a slot array is NULL, so the state
- * and conv arrays can be pools of per-request rows ("Kimi K3: Architecture and
- * SGLang Day-0 Support", "SGLang's day-0 adaptations": per-request state that
- * can be snapshotted and restored).  Reading a prefix checkpoint row and
- * writing another row is a copy-on-write fork; a row written by one sequence
- * must not be read or written by another sequence of the same call.
- * A zero-length sequence copies state and cache from its in row to its out row.
+ * and conv arrays can be pools of per-request rows.  Reading a read-only prefix
+ * checkpoint row and writing the request's own row is the copy-on-write fork of
+ * "Kimi K3: Architecture and SGLang Day-0 Support", section "RadixAttention:
+ * prefix caching for KDA state".  A row written by one sequence must not be
+ * read or written by another sequence of the same call.  A zero-length
+ * sequence copies state and cache from its in row to its out row.
  * Speculative verification runs draft tokens from the committed rows with
- * state_out and conv_out NULL, then replays the accepted tokens in place.
+ * state_out and conv_out NULL, then replays the accepted tokens in place (the
+ * replay of accepted inputs in "Inside Kimi K3: How KDA, AttnRes, and 896
+ * Experts Work", section "What could go wrong").
  */
 typedef struct {
     int32_t num_seqs;             /* N > 0 */

@@ -1,8 +1,9 @@
 """GPU parity of the serving-state features against the fp64 oracle, through the C ABI:
 slot-indexed state and conv-cache pools in prefill, copy-on-write forks from read-only
-checkpoints in prefill and decode, and speculative verification of draft tokens followed
-by a replay of the accepted ones ("Kimi K3: Architecture and SGLang Day-0 Support",
-"SGLang's day-0 adaptations": per-request state that can be snapshotted and restored).
+checkpoints in prefill and decode ("Kimi K3: Architecture and SGLang Day-0 Support",
+section "RadixAttention: prefix caching for KDA state"), and speculative verification of
+draft tokens followed by a replay of the accepted ones ("Inside Kimi K3: How KDA, AttnRes,
+and 896 Experts Work", section "What could go wrong").
 
 The oracle has no notion of pools: it runs on the rows a call reads (gathered on the host),
 and the pool rows a call writes are compared with its results.  Rows a call does not write

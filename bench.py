@@ -155,6 +155,85 @@ def run_extra_workloads(kda, W, dev, stream, log, algo="auto") -> dict:
     return out
 
 
+def run_serving_workloads(kda, dev, stream, log, H=96, B=256, drafts=4) -> dict:
+    """Serving-state calls on synthetic device inputs (seeded torch draws with the
+    workloads' value ranges): a copy-on-write decode step (B requests read checkpoint rows
+    of a state pool and write other rows), and one speculative round: verification of
+    `drafts` tokens per request from the committed rows (nothing written), then an
+    in-place replay of accepted prefixes of random length 0 .. drafts."""
+    import torch
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    bf = torch.bfloat16
+
+    def normal(*shape, std=1.0, dtype=bf):
+        return (torch.randn(*shape, generator=gen, device=dev) * std).to(dtype)
+
+    def gates(*shape):
+        la = -5.0 * torch.sigmoid(torch.randn(*shape, D, generator=gen, device=dev))
+        beta = torch.sigmoid(torch.randn(*shape, generator=gen, device=dev))
+        return la.contiguous(), beta.contiguous()
+
+    out = {}
+    rows = 2 * B
+    pool = normal(rows, H, D, D, std=0.02, dtype=torch.float32)
+    conv = normal(rows, 3, 3, H * D)
+    cw = normal(3, H * D, 4, std=0.5, dtype=torch.float32)
+    perm = torch.randperm(rows, generator=gen, device=dev).to(torch.int32)
+    s_in, s_out = perm[:B].contiguous(), perm[B:].contiguous()
+    q, k, v, g = (normal(B, H, D) for _ in range(4))
+    la, beta = gates(B, H)
+    o = torch.empty((B, H, D), dtype=bf, device=dev)
+    cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", prologue=True, epilogue=True)
+
+    def cow():
+        kda.decode_step(q, k, v, la, beta, pool, g=g, conv_w=cw, conv_state=conv, slots=s_in,
+                        slots_out=s_out, o=o, cfg=cfg, stream=stream)
+
+    cow()
+    ms, _ = time_events(cow, 10, stream)
+    out["decode_copy_on_write"] = {"requests": B, "heads": H, "ms": ms,
+                                   "state_GBps": 2 * B * H * D * D * 4 / (ms * 1e-3) / 1e9}
+    log(f"decode copy-on-write: {ms:.4f} ms, {out['decode_copy_on_write']['state_GBps']:.0f} GB/s of state")
+
+    T = B * drafts
+    dq, dk, dv, dg = (normal(T, H, D) for _ in range(4))
+    dla, dbeta = gates(T, H)
+    cu = torch.arange(0, T + 1, drafts, dtype=torch.int32, device=dev)
+    acc = torch.randint(0, drafts + 1, (B,), generator=gen, device=dev)
+    cu_acc = torch.zeros(B + 1, dtype=torch.int32, device=dev)
+    cu_acc[1:] = torch.cumsum(acc, 0).to(torch.int32)
+    Ta = int(cu_acc[-1].item())
+    idx = torch.cat([torch.arange(i * drafts, i * drafts + int(a), device=dev) for i, a in enumerate(acc.tolist())])
+    aq, ak, av, ag = (t[idx].contiguous() for t in (dq, dk, dv, dg))
+    ala, abeta = dla[idx].contiguous(), dbeta[idx].contiguous()
+    o_ver = torch.empty((T, H, D), dtype=bf, device=dev)
+    o_acc = torch.empty((max(Ta, 1), H, D), dtype=bf, device=dev)[:Ta]
+    ws = torch.empty(max(kda.workspace_size(cfg, B, T), 1), dtype=torch.uint8, device=dev)
+    slots = s_in
+
+    def verify():
+        kda.prefill(dq, dk, dv, dla, dbeta, cu, g=dg, conv_w=cw, conv_in=conv, state_in=pool, o=o_ver,
+                    state_in_slots=slots, workspace=ws, cfg=cfg, return_state=False, return_conv=False,
+                    stream=stream)
+
+    def replay():
+        kda.prefill(aq, ak, av, ala, abeta, cu_acc, g=ag, conv_w=cw, conv_in=conv, conv_out=conv,
+                    state_in=pool, state_out=pool, o=o_acc, state_in_slots=slots, state_out_slots=slots,
+                    workspace=ws, cfg=cfg, stream=stream)
+
+    verify()
+    vms, _ = time_events(verify, 10, stream)
+    rms_, _ = time_events(replay, 10, stream)
+    out["speculative_round"] = {"requests": B, "heads": H, "draft_tokens": drafts, "accepted_tokens": Ta,
+                                "verify_ms": vms, "replay_ms": rms_,
+                                "verified_tokens_per_s": T / (vms * 1e-3)}
+    log(f"speculative round: verify {T} tokens {vms:.3f} ms, replay {Ta} tokens {rms_:.3f} ms")
+    del pool, conv
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_events(fn, steps: int, stream):
     """Mean ms of fn() over `steps` calls, from HIP events recorded on `stream`."""
     import torch
@@ -308,7 +387,10 @@ def main() -> int:
         log(f"oracle: {L0} tokens x {H} heads in {ct:.1f}s on {threads} threads")
 
     traffic = load_traffic(args.traffic)
-    extra = run_extra_workloads(kda, W, dev, stream, log, args.algo) if args.extra_workloads else None
+    extra = None
+    if args.extra_workloads:
+        extra = run_extra_workloads(kda, W, dev, stream, log, args.algo)
+        extra.update(run_serving_workloads(kda, dev, stream, log))
 
     res = {
         "metric": "KDA prefill tokens/sec (H=96,d=128) + decode state GB/s at B=256",

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 HEAD_DIM = 128
 F32, BF16 = 0, 1
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2, "chunked_throughput": 3, "chunked_latency": 4}
+GATES = {"log_alpha": 0, "lowrank": 1}
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 
 EXPORTS = ("kda_config_init", "kda_prefill_workspace_size", "kda_prefill",
@@ -42,7 +43,8 @@ class Config(ctypes.Structure):
                 ("io_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("prologue", ctypes.c_int32), ("epilogue", ctypes.c_int32),
                 ("algo", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+                ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("gate", ctypes.c_int32), ("gate_rank", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -53,14 +55,15 @@ class PrefillArgs(ctypes.Structure):
                 ("q", _vp), ("k", _vp), ("v", _vp), ("log_alpha", _vp), ("beta", _vp), ("g", _vp),
                 ("conv_w", _vp), ("conv_in", _vp), ("conv_out", _vp), ("rms_w", _vp),
                 ("state_in", _vp), ("state_out", _vp), ("o", _vp), ("workspace", _vp),
-                ("workspace_bytes", ctypes.c_size_t), ("state_in_slots", _vp), ("state_out_slots", _vp)]
+                ("workspace_bytes", ctypes.c_size_t), ("state_in_slots", _vp), ("state_out_slots", _vp),
+                ("gate_z", _vp), ("gate_w", _vp), ("gate_bias", _vp), ("gate_a", _vp)]
 
 
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("q", _vp), ("k", _vp), ("v", _vp),
                 ("log_alpha", _vp), ("beta", _vp), ("g", _vp), ("conv_w", _vp),
                 ("conv_state", _vp), ("rms_w", _vp), ("state", _vp), ("slots", _vp), ("o", _vp),
-                ("slots_out", _vp)]
+                ("slots_out", _vp), ("gate_z", _vp), ("gate_w", _vp), ("gate_bias", _vp), ("gate_a", _vp)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -103,7 +106,7 @@ def _check(status: int) -> None:
 def config(num_heads: int, io_dtype: str = "bf16", out_dtype: Optional[str] = None,
            prologue: bool = True, epilogue: bool = True, algo: str = "auto",
            scale: Optional[float] = None, l2_eps: float = 1e-6, rms_eps: float = 1e-6,
-           head_dim: int = HEAD_DIM) -> Config:
+           head_dim: int = HEAD_DIM, gate: str = "log_alpha", gate_rank: int = 128) -> Config:
     c = Config()
     lib().kda_config_init(ctypes.byref(c), num_heads)
     c.head_dim = head_dim
@@ -115,6 +118,8 @@ def config(num_heads: int, io_dtype: str = "bf16", out_dtype: Optional[str] = No
     c.scale = 1.0 / math.sqrt(head_dim) if scale is None else float(scale)
     c.l2_eps = float(l2_eps)
     c.rms_eps = float(rms_eps)
+    c.gate = GATES[gate]
+    c.gate_rank = int(gate_rank)
     return c
 
 
@@ -152,6 +157,15 @@ def _expect(t, name: str, dtype, shape=None) -> None:
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _expect_gate(cfg, z, w, bias, a, T, H, io_t) -> None:
+    import torch
+    r = cfg.gate_rank
+    _expect(z, "gate_z", io_t, (T, r))
+    _expect(w, "gate_w", io_t, (H * HEAD_DIM, r))
+    _expect(bias, "gate_bias", torch.float32, (H * HEAD_DIM,))
+    _expect(a, "gate_a", torch.float32, (H,))
+
+
 def workspace_size(cfg: Config, num_seqs: int, total_tokens: int) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().kda_prefill_workspace_size(ctypes.byref(cfg), num_seqs, total_tokens, ctypes.byref(n)))
@@ -160,17 +174,22 @@ def workspace_size(cfg: Config, num_seqs: int, total_tokens: int) -> int:
 
 def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_in=None,
             conv_out=None, rms_w=None, state_in=None, state_out=None, o=None, workspace=None,
-            state_in_slots=None, state_out_slots=None,
-            cfg: Optional[Config] = None, return_state: bool = True, return_conv: bool = True,
+            state_in_slots=None, state_out_slots=None, gate_z=None, gate_w=None, gate_bias=None,
+            gate_a=None, cfg: Optional[Config] = None, return_state: bool = True, return_conv: bool = True,
             stream=None, **cfg_kwargs) -> Tuple[object, object, object]:
     """kda_prefill on torch tensors.  q, k, v, g: [T, H, 128]; log_alpha [T, H, 128] fp32;
     beta [T, H] fp32; cu_seqlens int32 [N+1] on the device.  Missing outputs are allocated.
     With state_in_slots / state_out_slots (int32 [N] on the device) the state and conv arrays
     are pools of rows [rows, H, 128, 128] / [rows, 3, 3, H*128] and sequence n reads row
     state_in_slots[n] and writes row state_out_slots[n]; outputs are then not allocated.
+    With the low-rank gate (cfg.gate == "lowrank", or gate_z given) log_alpha may be None and
+    gate_z [T, r], gate_w [H*128, r] (io dtype), gate_bias [H*128] and gate_a [H] (fp32) are used.
     Returns (o, state_out, conv_out)."""
     import torch
     T, H = q.shape[0], q.shape[1]
+    if cfg is None and gate_z is not None:
+        cfg_kwargs.setdefault("gate", "lowrank")
+        cfg_kwargs.setdefault("gate_rank", gate_z.shape[1])
     N = cu_seqlens.shape[0] - 1
     if cfg is None:
         io = "bf16" if q.dtype == torch.bfloat16 else "f32"
@@ -185,6 +204,7 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g)):
         _expect(t, name, io_t, (T, H, D))
     _expect(log_alpha, "log_alpha", torch.float32, (T, H, D))
+    _expect_gate(cfg, gate_z, gate_w, gate_bias, gate_a, T, H, io_t)
     _expect(beta, "beta", torch.float32, (T, H))
     _expect(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
     _expect(conv_w, "conv_w", torch.float32, (3, H * D, 4))
@@ -219,19 +239,23 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.state_in_slots, a.state_out_slots = _ptr(state_in_slots), _ptr(state_out_slots)
+    a.gate_z, a.gate_w, a.gate_bias, a.gate_a = _ptr(gate_z), _ptr(gate_w), _ptr(gate_bias), _ptr(gate_a)
     _check(lib().kda_prefill(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
     return o, state_out, conv_out
 
 
 def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_state=None,
-                rms_w=None, slots=None, slots_out=None, o=None, cfg: Optional[Config] = None,
-                stream=None, **cfg_kwargs):
+                rms_w=None, slots=None, slots_out=None, o=None, gate_z=None, gate_w=None,
+                gate_bias=None, gate_a=None, cfg: Optional[Config] = None, stream=None, **cfg_kwargs):
     """kda_decode_step on torch tensors: one token per request, q, k, v, g [B, H, 128];
     state [rows, H, 128, 128] and conv_state [rows, 3, 3, H*128] are pools updated in place:
     request b reads row slots[b] (b when None) and writes row slots_out[b] (its read row
     when None).  Returns o [B, H, 128]."""
     import torch
     B, H, D = q.shape
+    if cfg is None and gate_z is not None:
+        cfg_kwargs.setdefault("gate", "lowrank")
+        cfg_kwargs.setdefault("gate_rank", gate_z.shape[1])
     if cfg is None:
         io = "bf16" if q.dtype == torch.bfloat16 else "f32"
         cfg_kwargs.setdefault("io_dtype", io)
@@ -244,6 +268,7 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g)):
         _expect(t, name, io_t, (B, H, D))
     _expect(log_alpha, "log_alpha", torch.float32, (B, H, D))
+    _expect_gate(cfg, gate_z, gate_w, gate_bias, gate_a, B, H, io_t)
     _expect(beta, "beta", torch.float32, (B, H))
     n_slots = state.shape[0]
     _expect(state, "state", torch.float32, (n_slots, H, D, D))
@@ -267,6 +292,7 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
     a.conv_w, a.conv_state, a.rms_w = _ptr(conv_w), _ptr(conv_state), _ptr(rms_w)
     a.state, a.slots, a.o = _ptr(state), _ptr(slots), _ptr(o)
     a.slots_out = _ptr(slots_out)
+    a.gate_z, a.gate_w, a.gate_bias, a.gate_a = _ptr(gate_z), _ptr(gate_w), _ptr(gate_bias), _ptr(gate_a)
     _check(lib().kda_decode_step(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
     return o
 

@@ -53,6 +53,9 @@ kda_status check_config(const kda_config *cfg) {
     if ((cfg->prologue != 0 && cfg->prologue != 1) || (cfg->epilogue != 0 && cfg->epilogue != 1))
         return KDA_ERR_INVALID_ARGUMENT;
     if (!valid_algo(cfg->algo)) return KDA_ERR_INVALID_ARGUMENT;
+    if (cfg->gate != KDA_GATE_LOG_ALPHA && cfg->gate != KDA_GATE_LOWRANK) return KDA_ERR_INVALID_ARGUMENT;
+    if (cfg->gate == KDA_GATE_LOWRANK && (cfg->gate_rank < 32 || cfg->gate_rank > 128 || cfg->gate_rank % 32 != 0))
+        return KDA_ERR_UNSUPPORTED;
     if (!isfinite(cfg->scale) || !(cfg->l2_eps >= 0.f) || !(cfg->rms_eps >= 0.f) ||
         !isfinite(cfg->l2_eps) || !isfinite(cfg->rms_eps))
         return KDA_ERR_INVALID_ARGUMENT;
@@ -66,6 +69,26 @@ bool ok_ptr(const void *p, bool required) {
 }
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+// Gate inputs: log alpha for KDA_GATE_LOG_ALPHA, the low-rank factors for KDA_GATE_LOWRANK.
+bool ok_gate(const kda_config *cfg, const float *log_alpha, const void *z, const void *w, const float *bias,
+             const float *a, bool needed) {
+    const bool low = cfg->gate == KDA_GATE_LOWRANK;
+    return ok_ptr(log_alpha, needed && !low) && ok_ptr(z, needed && low) && ok_ptr(w, needed && low) &&
+           ok_ptr(bias, needed && low) && ok_ptr(a, needed && low);
+}
+
+void set_gate(LayerParams &p, const kda_config *cfg, const float *log_alpha, const void *z, const void *w,
+              const float *bias, const float *a) {
+    p.gate = cfg->gate;
+    p.gate_rank = cfg->gate_rank;
+    const bool low = cfg->gate == KDA_GATE_LOWRANK;
+    p.log_alpha = low ? nullptr : log_alpha;
+    p.gate_z = low ? z : nullptr;
+    p.gate_w = low ? w : nullptr;
+    p.gate_bias = low ? bias : nullptr;
+    p.gate_a = low ? a : nullptr;
+}
 
 }  // namespace
 
@@ -98,6 +121,8 @@ void kda_config_init(kda_config *cfg, int32_t num_heads) {
     cfg->scale = 1.0f / sqrtf(static_cast<float>(D));
     cfg->l2_eps = 1e-6f;
     cfg->rms_eps = 1e-6f;
+    cfg->gate = KDA_GATE_LOG_ALPHA;
+    cfg->gate_rank = 128;
 }
 
 int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs) {
@@ -127,7 +152,8 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     if (static_cast<int64_t>(a->num_seqs) * H > 0x7fffffffLL) return KDA_ERR_UNSUPPORTED;
     const bool tok = a->total_tokens > 0;
     if (!ok_ptr(a->cu_seqlens, true) || !ok_ptr(a->q, tok) || !ok_ptr(a->k, tok) ||
-        !ok_ptr(a->v, tok) || !ok_ptr(a->log_alpha, tok) || !ok_ptr(a->beta, tok) ||
+        !ok_ptr(a->v, tok) || !ok_gate(cfg, a->log_alpha, a->gate_z, a->gate_w, a->gate_bias, a->gate_a, tok) ||
+        !ok_ptr(a->beta, tok) ||
         !ok_ptr(a->o, tok) || !ok_ptr(a->g, tok && cfg->epilogue) ||
         !ok_ptr(a->conv_w, cfg->prologue != 0) || !ok_ptr(a->conv_in, false) ||
         !ok_ptr(a->conv_out, false) || !ok_ptr(a->rms_w, false) || !ok_ptr(a->state_in, false) ||
@@ -138,6 +164,11 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
 
     const int algo = kda_prefill_resolved_algo(cfg, a->num_seqs);
+    // the in-kernel low-rank gate runs on the matrix cores with bf16 factors (throughput
+    // variant) or on the VALU (recurrent kernel); the pipelined variant does not have it
+    if (cfg->gate == KDA_GATE_LOWRANK &&
+        (algo == KDA_ALGO_CHUNKED_LATENCY || (algo == KDA_ALGO_CHUNKED_THROUGHPUT && cfg->io_dtype != KDA_DTYPE_BF16)))
+        return KDA_ERR_UNSUPPORTED;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     int32_t *order = need > 0 ? static_cast<int32_t *>(a->workspace) : nullptr;
@@ -151,7 +182,8 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     p.cu_seqlens = a->cu_seqlens;
     p.order = order;
     p.q = a->q; p.k = a->k; p.v = a->v; p.g = cfg->epilogue ? a->g : nullptr;
-    p.log_alpha = a->log_alpha; p.beta = a->beta;
+    p.beta = a->beta;
+    set_gate(p, cfg, a->log_alpha, a->gate_z, a->gate_w, a->gate_bias, a->gate_a);
     p.conv_w = cfg->prologue ? a->conv_w : nullptr;
     p.rms_w = a->rms_w;
     p.conv_in = cfg->prologue ? a->conv_in : nullptr;
@@ -180,7 +212,8 @@ kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *a, void
     if (!a || a->batch <= 0) return KDA_ERR_INVALID_ARGUMENT;
     if (static_cast<int64_t>(a->batch) * cfg->num_heads > 0x7fffffffLL) return KDA_ERR_UNSUPPORTED;
     if (!ok_ptr(a->q, true) || !ok_ptr(a->k, true) || !ok_ptr(a->v, true) ||
-        !ok_ptr(a->log_alpha, true) || !ok_ptr(a->beta, true) || !ok_ptr(a->o, true) ||
+        !ok_gate(cfg, a->log_alpha, a->gate_z, a->gate_w, a->gate_bias, a->gate_a, true) ||
+        !ok_ptr(a->beta, true) || !ok_ptr(a->o, true) ||
         !ok_ptr(a->state, true) || !ok_ptr(a->g, cfg->epilogue != 0) ||
         !ok_ptr(a->conv_w, cfg->prologue != 0) || !ok_ptr(a->conv_state, cfg->prologue != 0) ||
         !ok_ptr(a->rms_w, false) || !ok_ptr(a->slots, false) || !ok_ptr(a->slots_out, false))
@@ -192,7 +225,8 @@ kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *a, void
     p.slots_in = a->slots;
     p.slots_out = a->slots_out ? a->slots_out : a->slots;
     p.q = a->q; p.k = a->k; p.v = a->v; p.g = cfg->epilogue ? a->g : nullptr;
-    p.log_alpha = a->log_alpha; p.beta = a->beta;
+    p.beta = a->beta;
+    set_gate(p, cfg, a->log_alpha, a->gate_z, a->gate_w, a->gate_bias, a->gate_a);
     p.conv_w = cfg->prologue ? a->conv_w : nullptr;
     p.rms_w = a->rms_w;
     p.conv_in = cfg->prologue ? a->conv_state : nullptr;

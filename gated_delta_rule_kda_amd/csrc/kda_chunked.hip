@@ -89,22 +89,27 @@ constexpr int OFF_EGC = OFF_BETA + C * 4;            // e^{G_C} fp32 [128]
 constexpr int OFF_CW = OFF_EGC + D * 4;              // conv weights fp32 [3 streams][4 taps][128]
 constexpr int OFF_RW = OFF_CW + 3 * 4 * D * 4;       // rms gain fp32 [128]
 constexpr int LDS_BYTES = OFF_RW + D * 4;
+// In-kernel low-rank gate: the chunk's z_down rows, bf16 [16][r + 8] (r <= 128)
+constexpr int ZPK = 128 + 8;
+constexpr int OFF_ZL = LDS_BYTES;
+constexpr int LDS_BYTES_LOWRANK = OFF_ZL + C * ZPK * 2;
 
 static_assert(C * RAW_ROW <= OFF_KRD - OFF_CUR, "staged rows must fit under the K / Q / Khat planes");
 static_assert(C * FPK * 4 <= 2 * PL_CD * 2, "output staging must fit in the KRD slot");
-static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per gfx950 CU");
+static_assert(2 * LDS_BYTES_LOWRANK <= 160 * 1024, "two workgroups per gfx950 CU");
 
 constexpr float LOG2E = 1.4426950408889634f;
 
 
 // The second bound is waves per SIMD: two workgroups of 8 waves per CU need four
 // (at most 128 VGPRs).
-template <typename IO, typename OUT>
+// LOWRANK: log alpha is formed in the kernel from the low-rank gate factors (bf16 io).
+template <typename IO, typename OUT, bool LOWRANK>
 __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     using IV = Vec8<IO>;   // eight-wide rows of the conv cache
     using I4 = Vec4<IO>;
     using IB = BufLoad4<IO>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LOWRANK ? LDS_BYTES_LOWRANK : LDS_BYTES];
     float *const RAW = reinterpret_cast<float *>(smem + OFF_HIST);  // [3 + 16][3][128]
     uint16_t *const KLh = reinterpret_cast<uint16_t *>(smem + OFF_KL);
     uint16_t *const QLh = reinterpret_cast<uint16_t *>(smem + OFF_QL);
@@ -120,6 +125,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     float *const EGC = reinterpret_cast<float *>(smem + OFF_EGC);
     float *const CW = reinterpret_cast<float *>(smem + OFF_CW);
     float *const RW = reinterpret_cast<float *>(smem + OFF_RW);
+    uint16_t *const ZL = reinterpret_cast<uint16_t *>(smem + OFF_ZL);  // LOWRANK only
 
     const int H = p.H;
     const int item = blockIdx.x;
@@ -158,6 +164,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     }
     if (tid < D) RW[tid] = p.rms_w ? p.rms_w[tid] : 1.0f;
     const float l2_eps = p.l2_eps * (LOG2E * LOG2E);
+    // low-rank gate: this lane's channel bias and e^{A_h} log2(e)
+    const float gbias = LOWRANK ? p.gate_bias[hD + col] : 0.0f;
+    const float gscale = LOWRANK ? __expf(p.gate_a[h]) * LOG2E : 0.0f;
 
     // ---- state slice in accumulator layout: S[t][i] = S(16t + 4lh + i, col) ----------------
     const int row_in = p.slots_in ? p.slots_in[n] : n;     // state_in / conv_in row
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     const char *qkv_base[3] = {static_cast<const char *>(p.q) + first * sizeof(IO),
                                static_cast<const char *>(p.k) + first * sizeof(IO),
                                static_cast<const char *>(p.v) + first * sizeof(IO)};
-    const char *la_base = reinterpret_cast<const char *>(p.log_alpha + first);
+    const char *la_base = LOWRANK ? nullptr : reinterpret_cast<const char *>(p.log_alpha + first);
     const char *beta_base = reinterpret_cast<const char *>(p.beta + static_cast<size_t>(t0) * H + h);
     const char *g_base = p.epilogue ? static_cast<const char *>(p.g) + first * sizeof(IO) : nullptr;
     char *o_base = static_cast<char *>(p.o) + first * sizeof(OUT);
@@ -202,10 +211,39 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 #pragma unroll
         for (int s = 0; s < 3; ++s)
             cur[s] = IB::load(rows_view(qkv_base[s] + cio, nrow, rowb_io, D * sizeof(IO)), off_io);
-        lar = BufLoad4<float>::load(rows_view(la_base + static_cast<size_t>(r0) * rowb_f, nrow, rowb_f, D * 4),
-                                    static_cast<uint32_t>(xt) * rowb_f + xc * 4u);
+        if (!LOWRANK)
+            lar = BufLoad4<float>::load(rows_view(la_base + static_cast<size_t>(r0) * rowb_f, nrow, rowb_f, D * 4),
+                                        static_cast<uint32_t>(xt) * rowb_f + xc * 4u);
         bet = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
             rows_view(beta_base + static_cast<size_t>(r0) * H * 4, nrow, H * 4, 4), static_cast<uint32_t>(xt * H) * 4u, 0, 0));
+    };
+    // Low-rank gate: z_down rows of a chunk (one chunk ahead, parked in ZL before the
+    // chunk starts) and this lane's W_up operand (the B operand of z_down W_up^T for
+    // the channels 16 wave .. 16 wave + 15, loaded during the previous epilogue).
+    const int rank = p.gate_rank;
+    const int zsteps = rank / 32;
+    uint2 zr = make_uint2(0u, 0u);
+    uint4 wb[4];
+    const char *z_base = LOWRANK ? static_cast<const char *>(p.gate_z) + static_cast<size_t>(t0) * rank * 2 : nullptr;
+    auto load_z = [&](int c) {
+        const int x = opaque(tid), xt = x >> 5, xc = (x & 31) * 4;
+        const int r0 = c * C, nrow = min(L, r0 + C) - r0;
+        const __amdgpu_buffer_rsrc_t v = rows_view(z_base + static_cast<size_t>(r0) * rank * 2, nrow, rank * 2, rank * 2);
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t z = __builtin_amdgcn_raw_buffer_load_b64(v, static_cast<uint32_t>(xt * rank + xc) * 2u, 0, 0);
+        zr = xc < rank ? make_uint2(z[0], z[1]) : make_uint2(0u, 0u);
+    };
+    auto park_z = [&]() {
+        const int x = opaque(tid), xt = x >> 5, xc = (x & 31) * 4;
+        if (xc < rank) *reinterpret_cast<uint2 *>(ZL + xt * ZPK + xc) = zr;
+    };
+    auto load_w = [&]() {
+        const int x = opaque(tid), xl = x & 63;
+        const uint16_t *w = static_cast<const uint16_t *>(p.gate_w) +
+                            (hD + (x >> 6) * 16 + (xl & 15)) * static_cast<size_t>(rank) + 8 * (xl >> 4);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            wb[st] = st < zsteps ? *reinterpret_cast<const uint4 *>(w + 32 * st) : make_uint4(0u, 0u, 0u, 0u);
     };
     auto load_gate = [&](int c) {
         const int x = opaque(tid);
@@ -217,6 +255,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     if (nchunks > 0) {
         load_current(0);
         load_gate(0);
+        if (LOWRANK) {
+            load_z(0);
+            load_w();
+        }
     }
     if (p.prologue && tid < 3 * CONV_HIST * 16) {
         // history of the first chunk: the given conv cache (oldest first) or zeros
@@ -243,17 +285,50 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             I4::unpack(cur[s], xr[s]);
             store4f(raw_t + s * D, xr[s]);
         }
-        {
+        if (LOWRANK) {
+            park_z();  // ZL was last read before the previous chunk's second barrier
+        } else {
             float la[4];
             Vec4<float>::unpack(lar, la);
 #pragma unroll
             for (int e = 0; e < 4; ++e) la[e] *= LOG2E;
             store4f(LA + et * D + ec0, la);
-            if ((tid & 31) == 0) BETA[et] = bet;
         }
+        if ((tid & 31) == 0) BETA[et] = bet;
+        if (LOWRANK) load_w();  // this lane's W_up operand, used right after the barrier
         __syncthreads();
 
         // ---- 2. conv4 + SiLU (+ L2 for q, k) from the staged rows; cumulative log-decay -------
+        if (LOWRANK) {
+            // log2(alpha) = -5 log2(e) sigmoid(e^{A_h} (z_down W_up^T + b)) for the chunk's
+            // tokens (rows) and this wave's 16 channels (columns), on the matrix cores (the
+            // bf16 factors multiply exactly and accumulate in fp32), then its running sum
+            // over the tokens: within the lane's 4 rows, then across the 4 row groups with
+            // two lane permutes.  Rows past the end of the sequence get log alpha = 0, so
+            // that they do not decay the carried state.
+            f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                if (st < zsteps) zacc = mma(*reinterpret_cast<const uint4 *>(ZL + ln * ZPK + 32 * st + 8 * lh), wb[st], zacc);
+            float run[4];
+            float acc_sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float t = (zacc[i] + gbias) * gscale;  // e^{A_h} (z + b) log2(e)
+                const float la2 = (-5.0f * LOG2E) * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
+                acc_sum += r0 + 4 * lh + i < L ? la2 : 0.0f;
+                run[i] = acc_sum;
+            }
+            const int lid = lane;
+            float x1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lid - 16) * 4, __builtin_bit_cast(int, acc_sum)));
+            x1 = acc_sum + (lh >= 1 ? x1 : 0.0f);
+            float x2 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lid - 32) * 4, __builtin_bit_cast(int, x1)));
+            x2 = x1 + (lh >= 2 ? x2 : 0.0f);
+            const float before = x2 - acc_sum;  // sum over the rows of the earlier row groups
+#pragma unroll
+            for (int i = 0; i < 4; ++i) LA[(4 * lh + i) * D + col] = run[i] + before;
+            if (lh == 3) EGC[col] = __builtin_amdgcn_exp2f(run[3] + before);
+        }
         float xq[4], xk[4], xv[4];
         {
             float *outs[3] = {xq, xk, xv};
@@ -309,7 +384,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 }
             }
         }
-        if (tid < D) {
+        if (!LOWRANK && tid < D) {
             const int c = tid;
             float g = 0.0f;
 #pragma unroll
@@ -528,7 +603,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                                             static_cast<uint32_t>(HD * sizeof(OUT)), D * sizeof(OUT)),
                                   static_cast<uint32_t>(et) * static_cast<uint32_t>(HD * sizeof(OUT)) + ec0 * sizeof(OUT), o);
         }
-        if (ch + 1 < nchunks) load_gate(ch + 1);
+        if (ch + 1 < nchunks) {
+            load_gate(ch + 1);
+            if (LOWRANK) load_z(ch + 1);
+        }
         // the next chunk's first two barriers order these LDS reads before any rewrite
     }
 
@@ -568,13 +646,24 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 template <typename IO, typename OUT>
 hipError_t launch(const LayerParams &p, hipStream_t s) {
     if (p.num_items == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+    hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename OUT>
+hipError_t launch_lowrank(const LayerParams &p, hipStream_t s) {
+    if (p.num_items == 0) return hipSuccess;
+    hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, true>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_chunked_throughput(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s) {
+    if (p.gate == KDA_GATE_LOWRANK) {  // bf16 io only (checked by the caller)
+        if (io_dtype != KDA_DTYPE_BF16) return hipErrorInvalidValue;
+        return out_dtype == KDA_DTYPE_BF16 ? launch_lowrank<uint16_t>(p, s) : launch_lowrank<float>(p, s);
+    }
     if (io_dtype == KDA_DTYPE_BF16)
         return out_dtype == KDA_DTYPE_BF16 ? launch<uint16_t, uint16_t>(p, s)
                                            : launch<uint16_t, float>(p, s);

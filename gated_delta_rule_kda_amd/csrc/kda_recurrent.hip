@@ -8,7 +8,9 @@
 //             lanes 128-255: v of channel t-128), L2 norms of q and k by wave
 //             reductions ("Kimi K3 - KDA layer" (OpenModelAtlas), conv/SiLU/L2
 //             steps; "Inside Kimi K3", short-convolution section)
-//   decay     S <- Diag(alpha) S, alpha per row = key channel
+//   decay     S <- Diag(alpha) S, alpha per row = key channel; alpha is given as
+//             log alpha or formed from the low-rank gate factors, alpha =
+//             exp(-5 sigmoid(e^{A_h} (z_down W_up^T + b))) ("Kimi K3 - KDA layer")
 //   predict   r = S^T k^  and  p = S^T q^ on the decayed state, in one pass
 //   write     S <- S + beta k^ (v - r)^T
 //   read      o~ = scale * S_new^T q^ = scale * (p + (q^.k^) beta (v - r))
@@ -36,6 +38,23 @@ __device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
     for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
     return x;
+}
+
+// log alpha of key channel c of head h at token t from the low-rank gate factors: an
+// fp32 dot product over the rank, then -5 sigmoid(e^{A_h} (z + b)).
+template <typename IO>
+__device__ __forceinline__ float lowrank_log_alpha(const LayerParams &p, int64_t t, int h, int c, float e_a) {
+    using IOT = IoTraits<IO>;
+    const int r = p.gate_rank;
+    const size_t zrow = static_cast<size_t>(t) * r;
+    const size_t wrow = (static_cast<size_t>(h) * D + c) * r;
+    float acc0 = 0.f, acc1 = 0.f;
+    for (int j = 0; j < r; j += 2) {
+        acc0 = fmaf(IOT::load(p.gate_z, zrow + j), IOT::load(p.gate_w, wrow + j), acc0);
+        acc1 = fmaf(IOT::load(p.gate_z, zrow + j + 1), IOT::load(p.gate_w, wrow + j + 1), acc1);
+    }
+    const float u = e_a * ((acc0 + acc1) + p.gate_bias[static_cast<size_t>(h) * D + c]);
+    return -5.0f * sigmoidf_(u);
 }
 
 template <typename IO, typename OUT>
@@ -120,6 +139,7 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) wr[jj] = p.rms_w ? p.rms_w[j0 + jj] : 1.0f;
 
+    const float e_a = p.gate_z ? __expf(p.gate_a[h]) : 0.0f;
     for (int64_t t = t0; t < t1; ++t) {
         const int buf = static_cast<int>((t - t0) & 1);
         const size_t row = (static_cast<size_t>(t) * H + h) * D;
@@ -158,7 +178,7 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
             }
             sh_v[buf][c] = xv;
             if (p.epilogue) sh_g[buf][c] = sigmoidf_(IOT::load(p.g, row + c));
-            sh_a[buf][c] = __expf(p.log_alpha[row + c]);
+            sh_a[buf][c] = __expf(p.gate_z ? lowrank_log_alpha<IO>(p, t, h, c, e_a) : p.log_alpha[row + c]);
             if (c == 0) sh_beta[buf] = p.beta[static_cast<size_t>(t) * H + h];
         }
         __syncthreads();

@@ -53,7 +53,7 @@ extern "C" {
 #endif
 
 #define KDA_HEAD_DIM 128
-#define KDA_ABI_VERSION 2u
+#define KDA_ABI_VERSION 3u
 
 /* Status codes. */
 typedef int32_t kda_status;
@@ -80,6 +80,15 @@ typedef int32_t kda_status;
 #define KDA_ALGO_CHUNKED_THROUGHPUT 3   /* 8-wave workgroups, two per compute unit */
 #define KDA_ALGO_CHUNKED_LATENCY 4      /* one 8-wave producer/consumer workgroup per compute unit */
 
+/* Where the decay comes from ("Kimi K3 - KDA layer" step list: z_down = x W_down,
+ * z = z_down W_up, alpha = exp(-5 sigmoid(e^A (z + b_alpha)))).  LOG_ALPHA: the
+ * caller passes log alpha per (token, head, key channel).  LOWRANK: the caller
+ * passes the rank-r projection z_down and the up-projection, bias and per-head A,
+ * and the kernels form log alpha = -5 sigmoid(e^{A_h} (z_down W_up^T + b)) on the
+ * fly, which removes the fp32 log alpha stream (512 B per token-head). */
+#define KDA_GATE_LOG_ALPHA 0
+#define KDA_GATE_LOWRANK 1
+
 typedef struct {
     int32_t num_heads;   /* H > 0 */
     int32_t head_dim;    /* must be 128 */
@@ -91,10 +100,13 @@ typedef struct {
     float scale;         /* read scale; 1/sqrt(128) in the layer */
     float l2_eps;        /* x / sqrt(sum x^2 + l2_eps) */
     float rms_eps;       /* x / sqrt(mean x^2 + rms_eps) */
+    int32_t gate;        /* KDA_GATE_* */
+    int32_t gate_rank;   /* r of KDA_GATE_LOWRANK: a multiple of 32 in [32, 128] */
 } kda_config;
 
 /* Fills *cfg with the layer's defaults for H heads: bf16 io and output,
- * prologue and epilogue on, AUTO algorithm, scale 1/sqrt(128), eps 1e-6. */
+ * prologue and epilogue on, AUTO algorithm, scale 1/sqrt(128), eps 1e-6,
+ * log alpha given (gate_rank 128 for when LOWRANK is chosen). */
 void kda_config_init(kda_config *cfg, int32_t num_heads);
 
 /* ------------------------------------------------------------------ prefill
@@ -120,7 +132,7 @@ typedef struct {
     const int32_t *cu_seqlens;    /* device [N+1]: cu[0] = 0, non-decreasing, cu[N] = total_tokens */
     int64_t total_tokens;         /* T >= 0 */
     const void *q, *k, *v;        /* [T][H][128] io_dtype */
-    const float *log_alpha;       /* [T][H][128] fp32, in [-5, 0] */
+    const float *log_alpha;       /* [T][H][128] fp32, in [-5, 0]; required iff gate == LOG_ALPHA */
     const float *beta;            /* [T][H] fp32, in [0, 1] */
     const void *g;                /* [T][H][128] io_dtype; required iff epilogue */
     const float *conv_w;          /* [3][H*128][4] fp32; required iff prologue */
@@ -134,6 +146,11 @@ typedef struct {
     size_t workspace_bytes;
     const int32_t *state_in_slots;   /* device [N] rows of state_in / conv_in, or NULL (row n) */
     const int32_t *state_out_slots;  /* device [N] rows of state_out / conv_out, or NULL (row n) */
+    /* gate == LOWRANK only (required then, ignored otherwise): */
+    const void *gate_z;           /* [T][r] io_dtype: z_down of each token (shared by the heads) */
+    const void *gate_w;           /* [H*128][r] io_dtype: W_up stored output-major (row c = channel c) */
+    const float *gate_bias;       /* [H*128] fp32: b_alpha */
+    const float *gate_a;          /* [H] fp32: A_h (the multiplier is e^{A_h}) */
 } kda_prefill_args;
 
 /* Bytes of device workspace kda_prefill needs for N sequences (it holds the
@@ -161,7 +178,7 @@ int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs);
 typedef struct {
     int32_t batch;                /* B > 0 requests */
     const void *q, *k, *v;        /* [B][H][128] io_dtype */
-    const float *log_alpha;       /* [B][H][128] fp32 */
+    const float *log_alpha;       /* [B][H][128] fp32; required iff gate == LOG_ALPHA */
     const float *beta;            /* [B][H] fp32 */
     const void *g;                /* [B][H][128] io_dtype; required iff epilogue */
     const float *conv_w;          /* [3][H*128][4] fp32; required iff prologue */
@@ -171,6 +188,10 @@ typedef struct {
     const int32_t *slots;         /* device [B] pool row each request reads, or NULL (row b) */
     void *o;                      /* [B][H][128] out_dtype */
     const int32_t *slots_out;     /* device [B] pool row each request writes, or NULL (its slots row) */
+    const void *gate_z;           /* gate == LOWRANK: [B][r] io_dtype (as in kda_prefill_args) */
+    const void *gate_w;           /* [H*128][r] io_dtype */
+    const float *gate_bias;       /* [H*128] fp32 */
+    const float *gate_a;          /* [H] fp32 */
 } kda_decode_args;
 
 kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *args, void *hip_stream);

@@ -239,6 +239,28 @@ def gen_decode(spec: DecodeSpec) -> Dict[str, np.ndarray]:
     return out
 
 
+def gen_gate(cu_seqlens, heads: int, rank: int = 128, seed: int = 1, io: str = "bf16",
+             first_seq: int = 0) -> Dict[str, np.ndarray]:
+    """Low-rank gate factors of the "Kimi K3 - KDA layer" step list for packed sequences:
+    z_down [T, r] per token (one generator per sequence, so slices of a workload match),
+    W_up stored output-major [H*128, r] with N(0, 1/r) entries (z_down W_up ~ N(0, 1)),
+    b_alpha [H*128] ~ N(0, 1) and A [H] ~ N(0.5, 0.2), so that e^A (z + b) spreads
+    log alpha over (-5, 0) around -2.5 like the log-alpha workloads.  bf16-rounded for
+    bf16 io (z_down, W_up); b_alpha and A are fp32."""
+    cu = np.asarray(cu_seqlens, np.int64)
+    T = int(cu[-1])
+    z = np.zeros((T, 1, rank), np.float32)
+    _fill_blocks(z, seed, 20, cu, lambda rng, shape: _normal32(rng, shape), bf16=(io == "bf16"),
+                 per_head=False, n0=first_seq)
+    rng = _rng(seed, 21)
+    w = (rng.standard_normal((heads * D, rank)) / np.sqrt(rank)).astype(np.float32)
+    if io == "bf16":
+        w = _bf16_inplace(w)
+    b = rng.standard_normal(heads * D).astype(np.float32)
+    a = (0.5 + 0.2 * rng.standard_normal(heads)).astype(np.float32)
+    return {"gate_z": z[:, 0], "gate_w": w, "gate_bias": b, "gate_a": a}
+
+
 def varlen_lengths(n_seqs: int = 64, mean: float = 8192.0, sigma: float = 1.0,
                    lo: int = 16, hi: int = 65536, seed: int = 4) -> List[int]:
     """Lognormal lengths whose distribution mean is `mean` (mu = ln mean - sigma^2/2)."""

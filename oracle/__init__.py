@@ -63,6 +63,25 @@ class Oracle:
         f.argtypes = ([ctypes.c_int] * 4 + [ctypes.POINTER(ctypes.c_int64)] + [_D] * 14 +
                       [ctypes.c_double] * 3 + [ctypes.c_int] * 2 + [_D] * 5 + [ctypes.c_int])
         self._run = f
+        g = lib.kda_oracle_lowrank_log_alpha
+        g.restype = ctypes.c_int
+        g.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [_D] * 5
+        self._gate = g
+
+    def lowrank_log_alpha(self, z, w, bias, a):
+        """log alpha [T, H, d] of the low-rank gate of the "Kimi K3 - KDA layer" step list,
+        alpha = exp(-5 sigmoid(e^{A_h} (z_down W_up + b_alpha))), from z_down [T, r],
+        W_up stored output-major [H*d, r], b_alpha [H*d] and A [H]."""
+        z, w, bias, a = (_f64(x) for x in (z, w, bias, a))
+        T, r = z.shape
+        H = a.shape[0]
+        d = w.shape[0] // H
+        assert w.shape == (H * d, r) and bias.shape == (H * d,)
+        out = np.zeros((T, H, d), np.float64)
+        rc = self._gate(T, H, d, r, _p(z), _p(w), _p(bias), _p(a), _p(out))
+        if rc != 0:
+            raise ValueError(f"kda_oracle_lowrank_log_alpha failed ({rc})")
+        return out
 
     # ------------------------------------------------------------------ prefill
     def prefill(self, q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None,
@@ -197,6 +216,10 @@ def default() -> Oracle:
 
 def prefill(*args, **kwargs):
     return default().prefill(*args, **kwargs)
+
+
+def lowrank_log_alpha(*args, **kwargs):
+    return default().lowrank_log_alpha(*args, **kwargs)
 
 
 def decode_step(*args, **kwargs):

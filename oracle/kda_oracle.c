@@ -66,6 +66,33 @@ typedef struct {
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
+/* The gate of [Atlas]'s step list, formed from its low-rank projection:
+ * z = z_down W_up, alpha = exp(-5 sigmoid(e^A (z + b_alpha))), returned as log alpha.
+ * Readings where the page is silent: A is one scalar per head (the per-head A_h of
+ * [Jawad], "Channel-wise decay, and the floor K3 puts under it"); W_up is passed
+ * output-major, w[c][j] = W_up[j][c] for output channel c = h * d + i; b_alpha is one
+ * value per output channel.  Plain loops in fp64, token by token.
+ *   z    [T][r]       the low-rank projection z_down of each token
+ *   w    [H*d][r]     W_up, row c = output channel c
+ *   b    [H*d]        b_alpha
+ *   a    [H]          A_h
+ *   out  [T][H][d]    log alpha */
+int kda_oracle_lowrank_log_alpha(int64_t T, int H, int d, int r, const double *z, const double *w,
+                                 const double *b, const double *a, double *out) {
+    if (T < 0 || H <= 0 || d <= 0 || r <= 0 || !z || !w || !b || !a || !out) return 1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h) {
+            const double ea = exp(a[h]);
+            for (int i = 0; i < d; ++i) {
+                const int64_t c = (int64_t)h * d + i;
+                double zc = 0.0;
+                for (int j = 0; j < r; ++j) zc += z[t * r + j] * w[c * r + j];
+                out[(t * H + h) * d + i] = -5.0 * sigmoid(ea * (zc + b[c]));
+            }
+        }
+    return 0;
+}
+
 /* One stream of the prologue for one token ([Atlas] conv + SiLU step):
  * y_c = sum_{j=0..3} w[c][j] * x_{t-j}[c],  a_c = y_c * sigmoid(y_c).
  * hist[0..2] holds x_{t-3}, x_{t-2}, x_{t-1} and is shifted to take x_t. */

@@ -369,4 +369,68 @@ def pin_heads_and_sequences_independent(orc):
             assert np.array_equal(s1[0, 0], s[n, h]), "head/sequence mixing in S"
 
 
+# --------------------------------------------------------------- low-rank gate
+# [Atlas] step list: z = z_down W_up, alpha = exp(-5 sigmoid(e^A (z + b_alpha))); [Jawad]
+# "Channel-wise decay, and the floor K3 puts under it": g = g_min sigmoid(e^{A_h} z) with
+# g_min = -5, so log alpha lies in (-5, 0).
+
+
+def pin_gate_zero_projection_is_half_floor(orc):
+    """z_down = 0 and b = 0: sigmoid(0) = 1/2, so log alpha = -2.5 for every A."""
+    rng = _rng(90)
+    H, d, r = 3, 4, 5
+    la = orc.lowrank_log_alpha(np.zeros((6, r)), rng.standard_normal((H * d, r)), np.zeros(H * d),
+                               rng.standard_normal(H))
+    _close(la, np.full((6, H, d), -2.5), 1e-15, "log alpha at zero projection")
+
+
+def pin_gate_floor_and_ceiling(orc):
+    """A large positive argument saturates at the floor log alpha = -5, a large negative
+    one at log alpha = 0 (no decay)."""
+    H, d, r = 2, 3, 4
+    z = np.zeros((2, r))
+    for b, want in ((1e3, -5.0), (-1e3, 0.0)):
+        la = orc.lowrank_log_alpha(z, np.zeros((H * d, r)), np.full(H * d, b), np.zeros(H))
+        _close(la, np.full((2, H, d), want), 1e-12, f"saturation at b = {b}")
+
+
+def pin_gate_sigmoid_symmetry(orc):
+    """sigmoid(-u) = 1 - sigmoid(u): negating z_down and b maps log alpha to -5 - log alpha."""
+    rng = _rng(91)
+    H, d, r = 2, 4, 6
+    z, w, b, a = rng.standard_normal((5, r)), rng.standard_normal((H * d, r)), rng.standard_normal(H * d), \
+        rng.standard_normal(H) * 0.5
+    la = orc.lowrank_log_alpha(z, w, b, a)
+    lb = orc.lowrank_log_alpha(-z, w, -b, a)
+    _close(la + lb, np.full_like(la, -5.0), 1e-13, "gate symmetry")
+    assert np.all(la < 0) and np.all(la > -5)
+
+
+def pin_gate_one_hot_selects_channel_and_head(orc):
+    """One-hot z_down (coordinate j) and a W_up whose only nonzero entry is output channel
+    c = h d + i, coordinate j: only that channel moves.  With e^{A_h} w = ln 3 the
+    sigmoid is 3/4 and log alpha = -3.75; head 1 has A = ln 2, so the same product
+    needs w = ln 3 / 2 there.  Every other channel stays at -2.5."""
+    H, d, r = 2, 3, 4
+    for h, i, j in ((0, 2, 1), (1, 0, 3)):
+        a = np.array([0.0, np.log(2.0)])
+        w = np.zeros((H * d, r))
+        w[h * d + i, j] = np.log(3.0) / np.exp(a[h])
+        z = np.zeros((1, r))
+        z[0, j] = 1.0
+        la = orc.lowrank_log_alpha(z, w, np.zeros(H * d), a)
+        want = np.full((1, H, d), -2.5)
+        want[0, h, i] = -3.75
+        _close(la, want, 1e-14, f"one-hot channel ({h}, {i}) via coordinate {j}")
+
+
+def pin_gate_bias_per_channel(orc):
+    """b_alpha shifts each output channel separately: with z_down = 0 and A = 0,
+    b_c = ln 3 gives log alpha = -3.75 and b_c = -ln 3 gives -1.25 (sigmoid = 1/4)."""
+    H, d, r = 2, 2, 3
+    b = np.array([np.log(3.0), -np.log(3.0), 0.0, np.log(3.0)])
+    la = orc.lowrank_log_alpha(np.zeros((1, r)), np.ones((H * d, r)), b, np.zeros(H))
+    _close(la.reshape(-1), np.array([-3.75, -1.25, -2.5, -3.75]), 1e-14, "bias per channel")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

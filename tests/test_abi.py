@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_sizes():
-    assert kda.abi_version() == 2
+    assert kda.abi_version() == 3
     assert kda.state_bytes(96) == 96 * 128 * 128 * 4
     # the pages' per-request figure: 69 KDA layers x 12 heads per GPU at TP=8 x 128^2 x fp32
     assert abs(69 * kda.state_bytes(12) / 1e6 - 54.26) < 0.01
@@ -46,6 +46,7 @@ def test_config_defaults():
     assert (c.num_heads, c.head_dim, c.io_dtype, c.out_dtype, c.prologue, c.epilogue, c.algo) == \
         (96, 128, kda.BF16, kda.BF16, 1, 1, 0)
     assert abs(c.scale - 128 ** -0.5) < 1e-7 and abs(c.l2_eps - 1e-6) < 1e-12
+    assert (c.gate, c.gate_rank) == (0, 128)
 
 
 def test_workspace_size():
@@ -133,6 +134,28 @@ def test_optional_pointers_follow_config():
     # off a null g / conv_w passes those checks and the call fails on the workspace
     c = kda.config(4, prologue=False, epilogue=False)
     assert _prefill(c, _args(g=None, conv_w=None, workspace=None)) == kda.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_lowrank_gate_arguments():
+    """With the low-rank gate log_alpha is optional and the four gate factors are
+    required; bad ranks and the variants without the in-kernel gate are refused."""
+    low = dict(gate_z=FAKE, gate_w=FAKE, gate_bias=FAKE, gate_a=FAKE)
+    ok = kda.ERR_WORKSPACE_TOO_SMALL  # the next check after the pointer checks
+    c = kda.config(4, gate="lowrank")
+    assert _prefill(c, _args(log_alpha=None, workspace=None, **low)) == ok
+    for f in low:
+        assert _prefill(c, _args(log_alpha=None, **dict(low, **{f: None}))) == kda.ERR_INVALID_ARGUMENT, f
+    # the log-alpha gate still requires log_alpha
+    assert _prefill(kda.config(4), _args(log_alpha=None, **low)) == kda.ERR_INVALID_ARGUMENT
+    for r in (0, 16, 48, 160):
+        assert _prefill(kda.config(4, gate="lowrank", gate_rank=r), _args(**low)) == kda.ERR_UNSUPPORTED, r
+    bad = kda.config(4)
+    bad.gate = 5
+    assert _prefill(bad, _args()) == kda.ERR_INVALID_ARGUMENT
+    one = dict(num_seqs=1, workspace=None, workspace_bytes=0)
+    assert _prefill(kda.config(4, gate="lowrank", algo="chunked_latency"), _args(**one, **low)) == kda.ERR_UNSUPPORTED
+    assert _prefill(kda.config(4, gate="lowrank", io_dtype="f32", algo="chunked"),
+                    _args(**one, **low)) == kda.ERR_UNSUPPORTED
 
 
 def test_decode_rejects_bad_arguments():

@@ -32,14 +32,16 @@ BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA
 D = 128
 
 
-def prefill_algorithmic_bytes(T: int, H: int, N: int, gate_rank: int = 0) -> int:
+def prefill_algorithmic_bytes(T: int, H: int, N: int, gate_rank: int = 0, head_gate: bool = False) -> int:
     """Bytes the prefill must move: per token-head q, k, v, g (bf16, 4 x 256 B),
     log alpha (fp32, 512 B), beta (4 B) and o (bf16, 256 B) = 1796 B; per
     (sequence, head) the 64 KiB fp32 final state; the fp32 conv weights
     (3 x H*128 x 4) and the bf16 conv cache out (N x 3 x 3 x H*128).  With the
     in-kernel low-rank gate of rank r (gate_rank > 0) log alpha is replaced by
-    z_down (bf16, T x r), W_up (bf16, H*128 x r), b_alpha and A."""
-    per_token_head = 4 * 2 * D + (0 if gate_rank else 4 * D) + 4 + 2 * D
+    z_down (bf16, T x r), W_up (bf16, H*128 x r), b_alpha and A.  With the scalar per-head
+    gate (head_gate) log alpha is one fp32 value per token-head (4 B)."""
+    la = 0 if gate_rank else (4 if head_gate else 4 * D)
+    per_token_head = 4 * 2 * D + la + 4 + 2 * D
     gate = T * gate_rank * 2 + H * D * gate_rank * 2 + H * D * 4 + H * 4 if gate_rank else 0
     return (T * H * per_token_head + N * H * D * D * 4 + 3 * H * D * 4 * 4 +
             N * 9 * H * D * 2 + gate)
@@ -193,6 +195,40 @@ def run_lowrank_gate_workload(kda, W, dev, stream, log, rank=128) -> dict:
     return {"prefill_4x4096_lowrank_gate": {"tokens": T, "rank": rank, "ms": ms, "tokens_per_s": T / (ms * 1e-3),
                                             "algorithmic_bytes": nb,
                                             "frac_of_hbm_roofline": nb / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}}
+
+
+def run_head_gate_workload(kda, W, dev, stream, log) -> dict:
+    """The 4 x 4096 x 96 prefill with one decay per (token, head) instead of one per key
+    channel (log alpha [T, H]: channel 0 of the channel-wise workload's values)."""
+    import torch
+    spec = W.workload("prefill_4x4096")
+    x = W.gen_prefill(spec)
+    bf = torch.bfloat16
+    T, H, N = x["q"].shape[0], spec.heads, len(spec.lens)
+    t = {n: torch.from_numpy(x[n]).to(dev).to(bf) for n in ("q", "k", "v", "g")}
+    la = torch.from_numpy(np.ascontiguousarray(x["log_alpha"][..., 0])).to(dev)
+    del x["log_alpha"]
+    beta = torch.from_numpy(x["beta"]).to(dev)
+    cu = torch.from_numpy(x["cu_seqlens"].astype(np.int32)).to(dev)
+    cw = torch.from_numpy(x["conv_w"]).to(dev)
+    cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", gate="head")
+    o = torch.empty((T, H, D), dtype=bf, device=dev)
+    s_out = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    c_out = torch.empty((N, 3, 3, H * D), dtype=bf, device=dev)
+    ws = torch.empty(max(kda.workspace_size(cfg, N, T), 1), dtype=torch.uint8, device=dev)
+
+    def run():
+        kda.prefill(t["q"], t["k"], t["v"], la, beta, cu, g=t["g"], conv_w=cw, o=o, state_out=s_out,
+                    conv_out=c_out, workspace=ws, cfg=cfg, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    ms, _ = time_events(run, 10, stream)
+    nb = prefill_algorithmic_bytes(T, H, N, head_gate=True)
+    log(f"prefill_4x4096 per-head gate: {ms:.3f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+    return {"prefill_4x4096_head_gate": {"tokens": T, "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                                         "algorithmic_bytes": nb,
+                                         "frac_of_hbm_roofline": nb / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}}
 
 
 def run_serving_workloads(kda, dev, stream, log, H=96, B=256, drafts=4) -> dict:
@@ -431,6 +467,7 @@ def main() -> int:
     if args.extra_workloads:
         extra = run_extra_workloads(kda, W, dev, stream, log, args.algo)
         extra.update(run_lowrank_gate_workload(kda, W, dev, stream, log))
+        extra.update(run_head_gate_workload(kda, W, dev, stream, log))
         extra.update(run_serving_workloads(kda, dev, stream, log))
 
     res = {

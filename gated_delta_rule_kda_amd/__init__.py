@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 HEAD_DIM = 128
 F32, BF16 = 0, 1
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2, "chunked_throughput": 3, "chunked_latency": 4}
-GATES = {"log_alpha": 0, "lowrank": 1}
+GATES = {"log_alpha": 0, "lowrank": 1, "head": 2}
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 
 EXPORTS = ("kda_config_init", "kda_prefill_workspace_size", "kda_prefill",
@@ -184,6 +184,7 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     state_in_slots[n] and writes row state_out_slots[n]; outputs are then not allocated.
     With the low-rank gate (cfg.gate == "lowrank", or gate_z given) log_alpha may be None and
     gate_z [T, r], gate_w [H*128, r] (io dtype), gate_bias [H*128] and gate_a [H] (fp32) are used.
+    With the scalar per-head gate (cfg.gate == "head") log_alpha is [T, H] fp32.
     Returns (o, state_out, conv_out)."""
     import torch
     T, H = q.shape[0], q.shape[1]
@@ -203,7 +204,7 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     D = q.shape[2]
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g)):
         _expect(t, name, io_t, (T, H, D))
-    _expect(log_alpha, "log_alpha", torch.float32, (T, H, D))
+    _expect(log_alpha, "log_alpha", torch.float32, (T, H) if cfg.gate == GATES["head"] else (T, H, D))
     _expect_gate(cfg, gate_z, gate_w, gate_bias, gate_a, T, H, io_t)
     _expect(beta, "beta", torch.float32, (T, H))
     _expect(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
@@ -250,7 +251,8 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
     """kda_decode_step on torch tensors: one token per request, q, k, v, g [B, H, 128];
     state [rows, H, 128, 128] and conv_state [rows, 3, 3, H*128] are pools updated in place:
     request b reads row slots[b] (b when None) and writes row slots_out[b] (its read row
-    when None).  Returns o [B, H, 128]."""
+    when None).  log_alpha is [B, H, 128] fp32, or [B, H] with cfg.gate == "head".
+    Returns o [B, H, 128]."""
     import torch
     B, H, D = q.shape
     if cfg is None and gate_z is not None:
@@ -267,7 +269,7 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
     io_t, out_t = _torch_dtype(cfg.io_dtype), _torch_dtype(cfg.out_dtype)
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g)):
         _expect(t, name, io_t, (B, H, D))
-    _expect(log_alpha, "log_alpha", torch.float32, (B, H, D))
+    _expect(log_alpha, "log_alpha", torch.float32, (B, H) if cfg.gate == GATES["head"] else (B, H, D))
     _expect_gate(cfg, gate_z, gate_w, gate_bias, gate_a, B, H, io_t)
     _expect(beta, "beta", torch.float32, (B, H))
     n_slots = state.shape[0]

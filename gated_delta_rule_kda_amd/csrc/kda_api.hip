@@ -53,7 +53,8 @@ kda_status check_config(const kda_config *cfg) {
     if ((cfg->prologue != 0 && cfg->prologue != 1) || (cfg->epilogue != 0 && cfg->epilogue != 1))
         return KDA_ERR_INVALID_ARGUMENT;
     if (!valid_algo(cfg->algo)) return KDA_ERR_INVALID_ARGUMENT;
-    if (cfg->gate != KDA_GATE_LOG_ALPHA && cfg->gate != KDA_GATE_LOWRANK) return KDA_ERR_INVALID_ARGUMENT;
+    if (cfg->gate != KDA_GATE_LOG_ALPHA && cfg->gate != KDA_GATE_LOWRANK && cfg->gate != KDA_GATE_HEAD)
+        return KDA_ERR_INVALID_ARGUMENT;
     if (cfg->gate == KDA_GATE_LOWRANK && (cfg->gate_rank < 32 || cfg->gate_rank > 128 || cfg->gate_rank % 32 != 0))
         return KDA_ERR_UNSUPPORTED;
     if (!isfinite(cfg->scale) || !(cfg->l2_eps >= 0.f) || !(cfg->rms_eps >= 0.f) ||
@@ -169,6 +170,7 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     if (cfg->gate == KDA_GATE_LOWRANK &&
         (algo == KDA_ALGO_CHUNKED_LATENCY || (algo == KDA_ALGO_CHUNKED_THROUGHPUT && cfg->io_dtype != KDA_DTYPE_BF16)))
         return KDA_ERR_UNSUPPORTED;
+    if (cfg->gate == KDA_GATE_HEAD && algo == KDA_ALGO_CHUNKED_LATENCY) return KDA_ERR_UNSUPPORTED;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     int32_t *order = need > 0 ? static_cast<int32_t *>(a->workspace) : nullptr;

@@ -88,7 +88,8 @@ constexpr int OFF_BETA = OFF_TM + 2 * PL_CC * 2;     // fp32 [16]
 constexpr int OFF_EGC = OFF_BETA + C * 4;            // e^{G_C} fp32 [128]
 constexpr int OFF_CW = OFF_EGC + D * 4;              // conv weights fp32 [3 streams][4 taps][128]
 constexpr int OFF_RW = OFF_CW + 3 * 4 * D * 4;       // rms gain fp32 [128]
-constexpr int LDS_BYTES = OFF_RW + D * 4;
+constexpr int OFF_GH = OFF_RW + D * 4;               // head gate: cumulative log2-decay [16], e^{G_C}
+constexpr int LDS_BYTES = OFF_GH + 32 * 4;
 // In-kernel low-rank gate: the chunk's z_down rows, bf16 [16][r + 8] (r <= 128)
 constexpr int ZPK = 128 + 8;
 constexpr int OFF_ZL = LDS_BYTES;
@@ -103,9 +104,17 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 // The second bound is waves per SIMD: two workgroups of 8 waves per CU need four
 // (at most 128 VGPRs).
-// LOWRANK: log alpha is formed in the kernel from the low-rank gate factors (bf16 io).
-template <typename IO, typename OUT, bool LOWRANK>
+// GATE (KDA_GATE_*): log alpha read per channel, formed in the kernel from the low-rank
+// gate factors (bf16 io), or read as one value per (token, head).
+template <typename IO, typename OUT, int GATE>
 __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
+    constexpr bool LOWRANK = GATE == KDA_GATE_LOWRANK;
+    // One decay per (token, head): Gamma is a row scale of the chunk's tokens, so it leaves
+    // the channel contractions.  The operand planes hold k^ and q^ unscaled (the k^ plane
+    // also serves as the Gram's B operand and, transposed, as Khat^T), and the factors are
+    // applied to the 16 x 16 Gram tiles and to the rows of the products: X = V - Diag(Gamma)
+    // (K^ S), O1 = Diag(Gamma) (Q^ S), S <- Gamma_C S + K^T (Diag(e^{G_C - G}) U).
+    constexpr bool HEADG = GATE == KDA_GATE_HEAD;
     using IV = Vec8<IO>;   // eight-wide rows of the conv cache
     using I4 = Vec4<IO>;
     using IB = BufLoad4<IO>;
@@ -125,6 +134,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     float *const EGC = reinterpret_cast<float *>(smem + OFF_EGC);
     float *const CW = reinterpret_cast<float *>(smem + OFF_CW);
     float *const RW = reinterpret_cast<float *>(smem + OFF_RW);
+    float *const GH = reinterpret_cast<float *>(smem + OFF_GH);  // head gate only
     uint16_t *const ZL = reinterpret_cast<uint16_t *>(smem + OFF_ZL);  // LOWRANK only
 
     const int H = p.H;
@@ -185,6 +195,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     // during the previous chunk's state products, so that their latency is hidden.
     typename I4::Raw cur[3];
     typename Vec4<float>::Raw lar;
+    float lah = 0.0f;  // head gate: this token's log alpha
     float bet = 0.0f;
     typename I4::Raw graw;
     // byte addresses of this (sequence, head)'s first row in each token-major tensor; a
@@ -195,7 +206,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     const char *qkv_base[3] = {static_cast<const char *>(p.q) + first * sizeof(IO),
                                static_cast<const char *>(p.k) + first * sizeof(IO),
                                static_cast<const char *>(p.v) + first * sizeof(IO)};
-    const char *la_base = LOWRANK ? nullptr : reinterpret_cast<const char *>(p.log_alpha + first);
+    const char *la_base = LOWRANK ? nullptr
+                          : HEADG ? reinterpret_cast<const char *>(p.log_alpha + static_cast<size_t>(t0) * H + h)
+                                  : reinterpret_cast<const char *>(p.log_alpha + first);
     const char *beta_base = reinterpret_cast<const char *>(p.beta + static_cast<size_t>(t0) * H + h);
     const char *g_base = p.epilogue ? static_cast<const char *>(p.g) + first * sizeof(IO) : nullptr;
     char *o_base = static_cast<char *>(p.o) + first * sizeof(OUT);
@@ -211,7 +224,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 #pragma unroll
         for (int s = 0; s < 3; ++s)
             cur[s] = IB::load(rows_view(qkv_base[s] + cio, nrow, rowb_io, D * sizeof(IO)), off_io);
-        if (!LOWRANK)
+        if (HEADG)
+            lah = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rows_view(la_base + static_cast<size_t>(r0) * H * 4, nrow, H * 4, 4), static_cast<uint32_t>(xt * H) * 4u, 0, 0));
+        else if (!LOWRANK)
             lar = BufLoad4<float>::load(rows_view(la_base + static_cast<size_t>(r0) * rowb_f, nrow, rowb_f, D * 4),
                                         static_cast<uint32_t>(xt) * rowb_f + xc * 4u);
         bet = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
@@ -287,6 +303,8 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         }
         if (LOWRANK) {
             park_z();  // ZL was last read before the previous chunk's second barrier
+        } else if (HEADG) {
+            if ((tid & 31) == 0) GH[et] = lah * LOG2E;
         } else {
             float la[4];
             Vec4<float>::unpack(lar, la);
@@ -384,7 +402,17 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 }
             }
         }
-        if (!LOWRANK && tid < D) {
+        if (HEADG) {
+            if (tid == 0) {
+                float g = 0.0f;
+#pragma unroll
+                for (int r = 0; r < C; ++r) {
+                    g += GH[r];
+                    GH[r] = g;
+                }
+                GH[C] = __builtin_amdgcn_exp2f(g);
+            }
+        } else if (!LOWRANK && tid < D) {
             const int c = tid;
             float g = 0.0f;
 #pragma unroll
@@ -403,7 +431,26 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 #pragma unroll
             for (int s = 0; s < 3; ++s) store4f(raw_t + (s - 3 * C) * D, xr[s]);
         }
-        {
+        if (HEADG) {
+            // k^ and q^ unscaled; the k^ split also fills the transposed Khat^T plane
+            const int at = et * OPK + cperm(ec0);
+            uint2 hi, lo;
+            split4(xq, hi, lo);
+            *reinterpret_cast<uint2 *>(QLh + at) = hi;
+            *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = lo;
+            split4(xk, hi, lo);
+            *reinterpret_cast<uint2 *>(KLh + at) = hi;
+            *reinterpret_cast<uint2 *>(KLh + PL_CD + at) = lo;
+            const uint32_t hw[4] = {hi.x, hi.x >> 16, hi.y, hi.y >> 16};
+            const uint32_t lw[4] = {lo.x, lo.x >> 16, lo.y, lo.y >> 16};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = ec0 + e;
+                KHTh[kht_pos(c, et)] = static_cast<uint16_t>(hw[e]);
+                KHTh[C + kht_pos(c, et)] = static_cast<uint16_t>(lw[e]);
+            }
+            store4f(VB + et * FPK + ec0, xv);
+        } else {
             float gl[4], egc[4];
             load4f(LA + et * D + ec0, gl);
             load4f(EGC + ec0, egc);
@@ -456,11 +503,20 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 const int ka = ln * OPK + 32 * s + 8 * lh;
                 const uint4 ah = *reinterpret_cast<const uint4 *>(Lh + ka);
                 const uint4 al = *reinterpret_cast<const uint4 *>(Lh + PL_CD + ka);
-                const uint4 bh = *reinterpret_cast<const uint4 *>(KRDh + ka);
-                const uint4 bl = *reinterpret_cast<const uint4 *>(KRDh + PL_CD + ka);
+                const uint16_t *Bp = HEADG ? KLh : KRDh;  // k^ / Gamma, or k^ for the head gate
+                const uint4 bh = *reinterpret_cast<const uint4 *>(Bp + ka);
+                const uint4 bl = *reinterpret_cast<const uint4 *>(Bp + PL_CD + ka);
                 acc2[s >> 1] = mma3(ah, al, bh, bl, acc2[s >> 1]);
             }
-            const f32x4_t acc = acc2[0] + acc2[1];
+            f32x4_t acc = acc2[0] + acc2[1];
+            if (HEADG) {  // row s, column j of the Gram tile times e^{G_s - G_j} (<= 1 for j <= s)
+                const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
+                const float gj = GH[ln];
+                acc[0] *= __builtin_amdgcn_exp2f(fminf(gr.x - gj, 0.0f));
+                acc[1] *= __builtin_amdgcn_exp2f(fminf(gr.y - gj, 0.0f));
+                acc[2] *= __builtin_amdgcn_exp2f(fminf(gr.z - gj, 0.0f));
+                acc[3] *= __builtin_amdgcn_exp2f(fminf(gr.w - gj, 0.0f));
+            }
             if (wave == 0) {
                 // T = (I + A)^{-1} Diag(beta) by forward substitution in fp32: lane 4j + r
                 // carries rows r, r+4, r+8, r+12 of column j of (I + A)^{-1}; step k
@@ -533,6 +589,16 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             X = mma3(kh, kl_, sh, sl, X);
             O1 = mma3(qh, ql_, sh, sl, O1);
         }
+        if (HEADG) {  // the row scales Gamma of Kbar = Diag(Gamma) K^ and Qbar = Diag(Gamma) Q^
+            const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
+            const float e4[4] = {__builtin_amdgcn_exp2f(gr.x), __builtin_amdgcn_exp2f(gr.y),
+                                 __builtin_amdgcn_exp2f(gr.z), __builtin_amdgcn_exp2f(gr.w)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                X[i] *= e4[i];
+                O1[i] *= e4[i];
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[i] = VB[(4 * lh + i) * FPK + col] - X[i];
         const Split4 Xs(X);
@@ -540,6 +606,12 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         // waves need before the barrier (they decay theirs after it)
         const bool late_decay = wave == 0;
         auto decay = [&]() {
+            if (HEADG) {
+                const float g = GH[C];  // e^{G_C}, one factor for the whole state
+#pragma unroll
+                for (int t = 0; t < 8; ++t) S[t] *= g;
+                return;
+            }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const float4 g4 = *reinterpret_cast<const float4 *>(EGC + 16 * t + 4 * lh);
@@ -559,7 +631,8 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             const uint2 Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh);
             const uint2 Ph = *reinterpret_cast<const uint2 *>(PMh + ln * OPT + 4 * lh);
             const uint2 Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + ln * OPT + 4 * lh);
-            const Split4 Us(mma16x2(Th, Tl, Xs.h, Xs.l, f32x4_t{0.f, 0.f, 0.f, 0.f}));
+            const f32x4_t Uf = mma16x2(Th, Tl, Xs.h, Xs.l, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            const Split4 Us(Uf);
             const f32x4_t O = mma16x2(Ph, Pl, Us.h, Us.l, O1);  // Qbar S + P U
 #pragma unroll
             for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = O[i];
@@ -567,8 +640,16 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             // Khat^T U with the products split as in mma16x2.  Rows of odd tiles hold their
             // two token pairs swapped (the plane's bank swizzle), so those tiles take the
             // U operand with its pairs swapped to match.
-            const uint4 ub_e = make_uint4(Us.h.x, Us.h.y, Us.h.x, Us.h.y), ul_e = make_uint4(Us.l.x, Us.l.y, 0u, 0u);
-            const uint4 ub_o = make_uint4(Us.h.y, Us.h.x, Us.h.y, Us.h.x), ul_o = make_uint4(Us.l.y, Us.l.x, 0u, 0u);
+            Split4 Uk = Us;
+            if (HEADG) {  // Khat^T U = K^T (Diag(e^{G_C - G}) U): scale the rows of U
+                const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
+                const float gc = GH[C - 1];
+                const float u4[4] = {Uf[0] * __builtin_amdgcn_exp2f(gc - gr.x), Uf[1] * __builtin_amdgcn_exp2f(gc - gr.y),
+                                     Uf[2] * __builtin_amdgcn_exp2f(gc - gr.z), Uf[3] * __builtin_amdgcn_exp2f(gc - gr.w)};
+                Uk = Split4(u4);
+            }
+            const uint4 ub_e = make_uint4(Uk.h.x, Uk.h.y, Uk.h.x, Uk.h.y), ul_e = make_uint4(Uk.l.x, Uk.l.y, 0u, 0u);
+            const uint4 ub_o = make_uint4(Uk.h.y, Uk.h.x, Uk.h.y, Uk.h.x), ul_o = make_uint4(Uk.l.y, Uk.l.x, 0u, 0u);
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int c = 16 * t + ln;
@@ -646,14 +727,17 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 template <typename IO, typename OUT>
 hipError_t launch(const LayerParams &p, hipStream_t s) {
     if (p.num_items == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+    if (p.gate == KDA_GATE_HEAD)
+        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_HEAD>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_LOG_ALPHA>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename OUT>
 hipError_t launch_lowrank(const LayerParams &p, hipStream_t s) {
     if (p.num_items == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, true>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+    hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOWRANK>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     return hipGetLastError();
 }
 

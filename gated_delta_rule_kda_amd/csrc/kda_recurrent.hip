@@ -9,8 +9,9 @@
 //             reductions ("Kimi K3 - KDA layer" (OpenModelAtlas), conv/SiLU/L2
 //             steps; "Inside Kimi K3", short-convolution section)
 //   decay     S <- Diag(alpha) S, alpha per row = key channel; alpha is given as
-//             log alpha or formed from the low-rank gate factors, alpha =
-//             exp(-5 sigmoid(e^{A_h} (z_down W_up^T + b))) ("Kimi K3 - KDA layer")
+//             log alpha (per channel, or one value per head), or formed from the
+//             low-rank gate factors, alpha = exp(-5 sigmoid(e^{A_h} (z_down W_up^T
+//             + b))) ("Kimi K3 - KDA layer")
 //   predict   r = S^T k^  and  p = S^T q^ on the decayed state, in one pass
 //   write     S <- S + beta k^ (v - r)^T
 //   read      o~ = scale * S_new^T q^ = scale * (p + (q^.k^) beta (v - r))
@@ -178,7 +179,10 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
             }
             sh_v[buf][c] = xv;
             if (p.epilogue) sh_g[buf][c] = sigmoidf_(IOT::load(p.g, row + c));
-            sh_a[buf][c] = __expf(p.gate_z ? lowrank_log_alpha<IO>(p, t, h, c, e_a) : p.log_alpha[row + c]);
+            const float la = p.gate_z ? lowrank_log_alpha<IO>(p, t, h, c, e_a)
+                             : p.gate == KDA_GATE_HEAD ? p.log_alpha[static_cast<size_t>(t) * H + h]
+                                                       : p.log_alpha[row + c];
+            sh_a[buf][c] = __expf(la);
             if (c == 0) sh_beta[buf] = p.beta[static_cast<size_t>(t) * H + h];
         }
         __syncthreads();

@@ -88,6 +88,11 @@ typedef int32_t kda_status;
  * fly, which removes the fp32 log alpha stream (512 B per token-head). */
 #define KDA_GATE_LOG_ALPHA 0
 #define KDA_GATE_LOWRANK 1
+/* HEAD: one decay per (token, head) shared by the 128 key channels, the scalar gate
+ * of Mamba-2 / Gated DeltaNet that KDA generalises ("Kimi K3's Architecture ...",
+ * section "Channel-wise decay, and the floor K3 puts under it"): log_alpha is
+ * [T][H].  A fast path: the decay factors leave the channel contractions. */
+#define KDA_GATE_HEAD 2
 
 typedef struct {
     int32_t num_heads;   /* H > 0 */
@@ -132,7 +137,7 @@ typedef struct {
     const int32_t *cu_seqlens;    /* device [N+1]: cu[0] = 0, non-decreasing, cu[N] = total_tokens */
     int64_t total_tokens;         /* T >= 0 */
     const void *q, *k, *v;        /* [T][H][128] io_dtype */
-    const float *log_alpha;       /* [T][H][128] fp32, in [-5, 0]; required iff gate == LOG_ALPHA */
+    const float *log_alpha;       /* [T][H][128] fp32 in [-5, 0] (gate LOG_ALPHA), or [T][H] (gate HEAD); else unused */
     const float *beta;            /* [T][H] fp32, in [0, 1] */
     const void *g;                /* [T][H][128] io_dtype; required iff epilogue */
     const float *conv_w;          /* [3][H*128][4] fp32; required iff prologue */
@@ -178,7 +183,7 @@ int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs);
 typedef struct {
     int32_t batch;                /* B > 0 requests */
     const void *q, *k, *v;        /* [B][H][128] io_dtype */
-    const float *log_alpha;       /* [B][H][128] fp32; required iff gate == LOG_ALPHA */
+    const float *log_alpha;       /* [B][H][128] fp32 (gate LOG_ALPHA) or [B][H] (gate HEAD); else unused */
     const float *beta;            /* [B][H] fp32 */
     const void *g;                /* [B][H][128] io_dtype; required iff epilogue */
     const float *conv_w;          /* [3][H*128][4] fp32; required iff prologue */

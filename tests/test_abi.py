@@ -192,3 +192,15 @@ def test_resolved_algo():
     bad = kda.config(4)
     bad.algo = 9
     assert L.kda_prefill_resolved_algo(ctypes.byref(bad), 1) == -1
+
+
+def test_head_gate_arguments():
+    """The scalar per-head gate reads log_alpha [T, H]: it is required, the low-rank
+    factors are ignored, and only the recurrent and throughput kernels take it."""
+    c = kda.config(4, gate="head")
+    assert c.gate == 2
+    assert _prefill(c, _args(log_alpha=None)) == kda.ERR_INVALID_ARGUMENT
+    assert _prefill(c, _args(workspace=None)) == kda.ERR_WORKSPACE_TOO_SMALL
+    one = dict(num_seqs=1, workspace=None, workspace_bytes=0)
+    assert _prefill(kda.config(4, gate="head", algo="chunked_latency"), _args(**one)) == kda.ERR_UNSUPPORTED
+    assert kda.resolved_algo(kda.config(4, gate="head"), 1) == "chunked_throughput"

@@ -67,20 +67,34 @@ class Oracle:
         g.restype = ctypes.c_int
         g.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int] + [_D] * 5
         self._gate = g
+        g2 = lib.kda_oracle_softplus_log_alpha
+        g2.restype = ctypes.c_int
+        g2.argtypes = g.argtypes
+        self._gate_softplus = g2
 
     def lowrank_log_alpha(self, z, w, bias, a):
         """log alpha [T, H, d] of the low-rank gate of the "Kimi K3 - KDA layer" step list,
         alpha = exp(-5 sigmoid(e^{A_h} (z_down W_up + b_alpha))), from z_down [T, r],
         W_up stored output-major [H*d, r], b_alpha [H*d] and A [H]."""
+        return self._lowrank(self._gate, z, w, bias, a)
+
+    def softplus_log_alpha(self, z, w, bias, a):
+        """log alpha [T, H, d] of Kimi Linear's unbounded gate,
+        log alpha = -e^{A_h} softplus(z_down W_up + b_alpha) (any value below 0), from the
+        same factors as lowrank_log_alpha."""
+        return self._lowrank(self._gate_softplus, z, w, bias, a)
+
+    @staticmethod
+    def _lowrank(fn, z, w, bias, a):
         z, w, bias, a = (_f64(x) for x in (z, w, bias, a))
         T, r = z.shape
         H = a.shape[0]
         d = w.shape[0] // H
         assert w.shape == (H * d, r) and bias.shape == (H * d,)
         out = np.zeros((T, H, d), np.float64)
-        rc = self._gate(T, H, d, r, _p(z), _p(w), _p(bias), _p(a), _p(out))
+        rc = fn(T, H, d, r, _p(z), _p(w), _p(bias), _p(a), _p(out))
         if rc != 0:
-            raise ValueError(f"kda_oracle_lowrank_log_alpha failed ({rc})")
+            raise ValueError(f"low-rank gate failed ({rc})")
         return out
 
     # ------------------------------------------------------------------ prefill
@@ -220,6 +234,10 @@ def prefill(*args, **kwargs):
 
 def lowrank_log_alpha(*args, **kwargs):
     return default().lowrank_log_alpha(*args, **kwargs)
+
+
+def softplus_log_alpha(*args, **kwargs):
+    return default().softplus_log_alpha(*args, **kwargs)
 
 
 def decode_step(*args, **kwargs):

@@ -66,19 +66,25 @@ typedef struct {
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
-/* The gate of [Atlas]'s step list, formed from its low-rank projection:
- * z = z_down W_up, alpha = exp(-5 sigmoid(e^A (z + b_alpha))), returned as log alpha.
- * Readings where the page is silent: A is one scalar per head (the per-head A_h of
- * [Jawad], "Channel-wise decay, and the floor K3 puts under it"); W_up is passed
- * output-major, w[c][j] = W_up[j][c] for output channel c = h * d + i; b_alpha is one
- * value per output channel.  Plain loops in fp64, token by token.
+/* The two low-rank gates.  Both read u = z_down W_up + b_alpha for output channel
+ * c = h * d + i, with W_up passed output-major (w[c][j] = W_up[j][c]), b_alpha one value
+ * per output channel and A one scalar per head (the per-head A_h of [Jawad],
+ * "Channel-wise decay, and the floor K3 puts under it"); these are readings where the
+ * pages are silent.  Plain loops in fp64, token by token.
  *   z    [T][r]       the low-rank projection z_down of each token
  *   w    [H*d][r]     W_up, row c = output channel c
  *   b    [H*d]        b_alpha
  *   a    [H]          A_h
- *   out  [T][H][d]    log alpha */
-int kda_oracle_lowrank_log_alpha(int64_t T, int H, int d, int r, const double *z, const double *w,
-                                 const double *b, const double *a, double *out) {
+ *   out  [T][H][d]    log alpha
+ * K3's gate ([Atlas] step list; [Jawad], same section): alpha = exp(-5 sigmoid(e^A u)),
+ * so log alpha lies in (-5, 0).
+ * Kimi Linear's gate, the unbounded log-decay that [Jawad]'s section contrasts with it:
+ * log alpha = -e^A softplus(u), softplus(u) = log(1 + e^u), any value in (-inf, 0).  For
+ * u > 0 softplus is evaluated as u + log(1 + e^-u), the same value without overflowing e^u. */
+static double softplus(double u) { return u > 0.0 ? u + log1p(exp(-u)) : log1p(exp(u)); }
+
+static int lowrank_gate(int64_t T, int H, int d, int r, const double *z, const double *w,
+                        const double *b, const double *a, int unbounded, double *out) {
     if (T < 0 || H <= 0 || d <= 0 || r <= 0 || !z || !w || !b || !a || !out) return 1;
     for (int64_t t = 0; t < T; ++t)
         for (int h = 0; h < H; ++h) {
@@ -87,10 +93,21 @@ int kda_oracle_lowrank_log_alpha(int64_t T, int H, int d, int r, const double *z
                 const int64_t c = (int64_t)h * d + i;
                 double zc = 0.0;
                 for (int j = 0; j < r; ++j) zc += z[t * r + j] * w[c * r + j];
-                out[(t * H + h) * d + i] = -5.0 * sigmoid(ea * (zc + b[c]));
+                const double u = zc + b[c];
+                out[(t * H + h) * d + i] = unbounded ? -ea * softplus(u) : -5.0 * sigmoid(ea * u);
             }
         }
     return 0;
+}
+
+int kda_oracle_lowrank_log_alpha(int64_t T, int H, int d, int r, const double *z, const double *w,
+                                 const double *b, const double *a, double *out) {
+    return lowrank_gate(T, H, d, r, z, w, b, a, 0, out);
+}
+
+int kda_oracle_softplus_log_alpha(int64_t T, int H, int d, int r, const double *z, const double *w,
+                                  const double *b, const double *a, double *out) {
+    return lowrank_gate(T, H, d, r, z, w, b, a, 1, out);
 }
 
 /* One stream of the prologue for one token ([Atlas] conv + SiLU step):

@@ -433,4 +433,63 @@ def pin_gate_bias_per_channel(orc):
     _close(la.reshape(-1), np.array([-3.75, -1.25, -2.5, -3.75]), 1e-14, "bias per channel")
 
 
+# ------------------------------------------------------ Kimi Linear's unbounded gate
+# [Jawad] "Channel-wise decay, and the floor K3 puts under it": Kimi Linear's log-decay
+# g = -e^A softplus(z) takes any value in (-inf, 0).
+
+
+def pin_softplus_gate_at_zero_is_ln2(orc):
+    """z_down = 0 and b = 0: softplus(0) = ln 2, so log alpha = -e^{A_h} ln 2, per head."""
+    rng = _rng(92)
+    H, d, r = 3, 4, 5
+    a = rng.standard_normal(H)
+    la = orc.softplus_log_alpha(np.zeros((2, r)), rng.standard_normal((H * d, r)), np.zeros(H * d), a)
+    want = np.broadcast_to((-np.exp(a) * np.log(2.0))[None, :, None], (2, H, d))
+    _close(la, want, 1e-15, "log alpha at zero argument")
+
+
+def pin_softplus_gate_closed_forms(orc):
+    """softplus(ln 3) = ln 4 and softplus(-ln 3) = ln(4/3); far out, softplus(u) -> u for
+    u = 800 (where e^u overflows fp64) and -> e^u for u = -50; the decay is unbounded:
+    e^A = 10 at u = 800 gives log alpha = -8000."""
+    H, d, r = 1, 4, 2
+    b = np.array([np.log(3.0), -np.log(3.0), 800.0, -50.0])
+    for a_h, ea in ((0.0, 1.0), (np.log(10.0), 10.0)):
+        la = orc.softplus_log_alpha(np.zeros((1, r)), np.zeros((H * d, r)), b, np.array([a_h]))
+        want = -ea * np.array([np.log(4.0), np.log(4.0 / 3.0), 800.0, np.exp(-50.0)])
+        _close(la.reshape(-1), want, 1e-14, f"closed forms at e^A = {ea}")
+
+
+def pin_softplus_gate_reflection(orc):
+    """softplus(u) - softplus(-u) = u: negating z_down and b changes log alpha by
+    -e^{A_h} (z_down W_up + b), with the projection taken as a numpy matrix product; and
+    e^{-softplus(-u)} = sigmoid(u) ties the gate to the logistic function."""
+    rng = _rng(93)
+    H, d, r = 2, 3, 6
+    z, w, b, a = rng.standard_normal((4, r)), rng.standard_normal((H * d, r)), rng.standard_normal(H * d), \
+        rng.standard_normal(H) * 0.5
+    la = orc.softplus_log_alpha(z, w, b, a)
+    lb = orc.softplus_log_alpha(-z, w, -b, a)
+    u = (z @ w.T + b).reshape(4, H, d)
+    ea = np.exp(a)[None, :, None]
+    _close(la - lb, -ea * u, 1e-12, "softplus reflection")
+    _close(np.exp(lb / ea), 1.0 / (1.0 + np.exp(-u)), 1e-12, "exp(-softplus(-u)) = sigmoid(u)")
+    assert np.all(la < 0)
+
+
+def pin_softplus_gate_one_hot_channel(orc):
+    """One-hot z_down and a single nonzero W_up entry move one output channel only: with
+    w = ln 3 there, that channel has softplus(ln 3) = ln 4, every other ln 2 (A = 0)."""
+    H, d, r = 2, 3, 4
+    for h, i, j in ((1, 1, 0), (0, 2, 3)):
+        w = np.zeros((H * d, r))
+        w[h * d + i, j] = np.log(3.0)
+        z = np.zeros((1, r))
+        z[0, j] = 1.0
+        la = orc.softplus_log_alpha(z, w, np.zeros(H * d), np.zeros(H))
+        want = np.full((1, H, d), -np.log(2.0))
+        want[0, h, i] = -np.log(4.0)
+        _close(la, want, 1e-14, f"one-hot channel ({h}, {i})")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -39,10 +39,14 @@ MUTANTS = [
     ("state_in_ignored", "memcpy(S, jb->s_in + ((size_t)n * H + h) * sdim, sdim * sizeof(double));",
      "memset(S, 0, sdim * sizeof(double));"),
     ("gate_w_transposed", "zc += z[t * r + j] * w[c * r + j];", "zc += z[t * r + j] * w[(j * H * d + c) % (H * d * r)];"),
-    ("gate_bias_sign", "sigmoid(ea * (zc + b[c]))", "sigmoid(ea * (zc - b[c]))"),
+    ("gate_bias_sign", "const double u = zc + b[c];", "const double u = zc - b[c];"),
     ("gate_a_not_exponentiated", "const double ea = exp(a[h]);", "const double ea = a[h];"),
     ("gate_a_wrong_head", "const double ea = exp(a[h]);", "const double ea = exp(a[0]);"),
-    ("gate_floor_not_five", "out[(t * H + h) * d + i] = -5.0 * sigmoid", "out[(t * H + h) * d + i] = -1.0 * sigmoid"),
+    ("gate_floor_not_five", "-5.0 * sigmoid(ea * u)", "-1.0 * sigmoid(ea * u)"),
+    ("softplus_a_inside", "-ea * softplus(u)", "-softplus(ea * u)"),
+    ("softplus_sign", "u + log1p(exp(-u))", "u - log1p(exp(-u))"),
+    ("softplus_naive_overflows", "u > 0.0 ? u + log1p(exp(-u)) : log1p(exp(u))", "log1p(exp(u))"),
+    ("softplus_is_sigmoid_branch", "log1p(exp(u)); }", "exp(u); }"),
 ]
 
 

@@ -160,13 +160,19 @@ def run_extra_workloads(kda, W, dev, stream, log, algo="auto") -> dict:
     return out
 
 
-def run_lowrank_gate_workload(kda, W, dev, stream, log, rank=128) -> dict:
+def run_lowrank_gate_workload(kda, W, dev, stream, log, rank=128, softplus=False, wild_every=0) -> dict:
     """The 4 x 4096 x 96 prefill with log alpha formed in the kernel from rank-`rank`
-    gate factors (the fp32 log alpha stream is not read)."""
+    gate factors (the fp32 log alpha stream is not read): K3's floored gate, or Kimi
+    Linear's unbounded softplus gate (softplus), with every `wild_every`-th head decaying
+    fast enough to take its chunks off the matrix cores."""
     import torch
     spec = W.workload("prefill_4x4096")
     x = W.gen_prefill(spec)
-    gate = W.gen_gate(x["cu_seqlens"], spec.heads, rank, seed=spec.seed)
+    if softplus:
+        wild = tuple(range(0, spec.heads, wild_every)) if wild_every else ()
+        gate = W.gen_softplus_gate(x["cu_seqlens"], spec.heads, rank, seed=spec.seed, wild_heads=wild)
+    else:
+        gate = W.gen_gate(x["cu_seqlens"], spec.heads, rank, seed=spec.seed)
     bf = torch.bfloat16
     T, H, N = x["q"].shape[0], spec.heads, len(spec.lens)
     t = {n: torch.from_numpy(x[n]).to(dev).to(bf) for n in ("q", "k", "v", "g")}
@@ -176,7 +182,8 @@ def run_lowrank_gate_workload(kda, W, dev, stream, log, rank=128) -> dict:
     cw = torch.from_numpy(x["conv_w"]).to(dev)
     gz, gw = (torch.from_numpy(gate[n]).to(dev).to(bf) for n in ("gate_z", "gate_w"))
     gb, ga = (torch.from_numpy(gate[n]).to(dev) for n in ("gate_bias", "gate_a"))
-    cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", gate="lowrank", gate_rank=rank)
+    cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", gate="lowrank_softplus" if softplus else "lowrank",
+                     gate_rank=rank)
     o = torch.empty((T, H, D), dtype=bf, device=dev)
     s_out = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
     c_out = torch.empty((N, 3, 3, H * D), dtype=bf, device=dev)
@@ -191,10 +198,10 @@ def run_lowrank_gate_workload(kda, W, dev, stream, log, rank=128) -> dict:
     torch.cuda.synchronize()
     ms, _ = time_events(run, 10, stream)
     nb = prefill_algorithmic_bytes(T, H, N, gate_rank=rank)
-    log(f"prefill_4x4096 low-rank gate (r={rank}): {ms:.3f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
-    return {"prefill_4x4096_lowrank_gate": {"tokens": T, "rank": rank, "ms": ms, "tokens_per_s": T / (ms * 1e-3),
-                                            "algorithmic_bytes": nb,
-                                            "frac_of_hbm_roofline": nb / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}}
+    name = "prefill_4x4096_" + (f"softplus_gate_wild{wild_every}" if softplus else "lowrank_gate")
+    log(f"{name} (r={rank}): {ms:.3f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+    return {name: {"tokens": T, "rank": rank, "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                   "algorithmic_bytes": nb, "frac_of_hbm_roofline": nb / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}}
 
 
 def run_head_gate_workload(kda, W, dev, stream, log) -> dict:
@@ -468,6 +475,8 @@ def main() -> int:
         extra = run_extra_workloads(kda, W, dev, stream, log, args.algo)
         extra.update(run_lowrank_gate_workload(kda, W, dev, stream, log))
         extra.update(run_head_gate_workload(kda, W, dev, stream, log))
+        extra.update(run_lowrank_gate_workload(kda, W, dev, stream, log, softplus=True))
+        extra.update(run_lowrank_gate_workload(kda, W, dev, stream, log, softplus=True, wild_every=8))
         extra.update(run_serving_workloads(kda, dev, stream, log))
 
     res = {

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 HEAD_DIM = 128
 F32, BF16 = 0, 1
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2, "chunked_throughput": 3, "chunked_latency": 4}
-GATES = {"log_alpha": 0, "lowrank": 1, "head": 2}
+GATES = {"log_alpha": 0, "lowrank": 1, "head": 2, "lowrank_softplus": 3, "log_alpha_unbounded": 4}
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 
 EXPORTS = ("kda_config_init", "kda_prefill_workspace_size", "kda_prefill",
@@ -184,7 +184,10 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     state_in_slots[n] and writes row state_out_slots[n]; outputs are then not allocated.
     With the low-rank gate (cfg.gate == "lowrank", or gate_z given) log_alpha may be None and
     gate_z [T, r], gate_w [H*128, r] (io dtype), gate_bias [H*128] and gate_a [H] (fp32) are used.
-    With the scalar per-head gate (cfg.gate == "head") log_alpha is [T, H] fp32.
+    gate "lowrank_softplus" takes the same factors and forms Kimi Linear's unbounded
+    log alpha = -e^A softplus(z_down W_up^T + b).  With the scalar per-head gate
+    (cfg.gate == "head") log_alpha is [T, H] fp32; with "log_alpha_unbounded" it is
+    [T, H, 128] with any value <= 0.
     Returns (o, state_out, conv_out)."""
     import torch
     T, H = q.shape[0], q.shape[1]

@@ -44,6 +44,11 @@ bool trace_enabled() {
     return on;
 }
 
+// the gates formed in the kernels from z_down, W_up, b and A
+bool lowrank_gate(const kda_config *cfg) {
+    return cfg->gate == KDA_GATE_LOWRANK || cfg->gate == KDA_GATE_LOWRANK_SOFTPLUS;
+}
+
 kda_status check_config(const kda_config *cfg) {
     if (!cfg) return KDA_ERR_INVALID_ARGUMENT;
     if (cfg->head_dim != D) return KDA_ERR_UNSUPPORTED;
@@ -53,9 +58,8 @@ kda_status check_config(const kda_config *cfg) {
     if ((cfg->prologue != 0 && cfg->prologue != 1) || (cfg->epilogue != 0 && cfg->epilogue != 1))
         return KDA_ERR_INVALID_ARGUMENT;
     if (!valid_algo(cfg->algo)) return KDA_ERR_INVALID_ARGUMENT;
-    if (cfg->gate != KDA_GATE_LOG_ALPHA && cfg->gate != KDA_GATE_LOWRANK && cfg->gate != KDA_GATE_HEAD)
-        return KDA_ERR_INVALID_ARGUMENT;
-    if (cfg->gate == KDA_GATE_LOWRANK && (cfg->gate_rank < 32 || cfg->gate_rank > 128 || cfg->gate_rank % 32 != 0))
+    if (cfg->gate < KDA_GATE_LOG_ALPHA || cfg->gate > KDA_GATE_LOG_ALPHA_UNBOUNDED) return KDA_ERR_INVALID_ARGUMENT;
+    if (lowrank_gate(cfg) && (cfg->gate_rank < 32 || cfg->gate_rank > 128 || cfg->gate_rank % 32 != 0))
         return KDA_ERR_UNSUPPORTED;
     if (!isfinite(cfg->scale) || !(cfg->l2_eps >= 0.f) || !(cfg->rms_eps >= 0.f) ||
         !isfinite(cfg->l2_eps) || !isfinite(cfg->rms_eps))
@@ -71,10 +75,11 @@ bool ok_ptr(const void *p, bool required) {
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
-// Gate inputs: log alpha for KDA_GATE_LOG_ALPHA, the low-rank factors for KDA_GATE_LOWRANK.
+// Gate inputs: log alpha for KDA_GATE_LOG_ALPHA and KDA_GATE_HEAD, the low-rank factors
+// for the two LOWRANK gates.
 bool ok_gate(const kda_config *cfg, const float *log_alpha, const void *z, const void *w, const float *bias,
              const float *a, bool needed) {
-    const bool low = cfg->gate == KDA_GATE_LOWRANK;
+    const bool low = lowrank_gate(cfg);
     return ok_ptr(log_alpha, needed && !low) && ok_ptr(z, needed && low) && ok_ptr(w, needed && low) &&
            ok_ptr(bias, needed && low) && ok_ptr(a, needed && low);
 }
@@ -83,7 +88,7 @@ void set_gate(LayerParams &p, const kda_config *cfg, const float *log_alpha, con
               const float *bias, const float *a) {
     p.gate = cfg->gate;
     p.gate_rank = cfg->gate_rank;
-    const bool low = cfg->gate == KDA_GATE_LOWRANK;
+    const bool low = lowrank_gate(cfg);
     p.log_alpha = low ? nullptr : log_alpha;
     p.gate_z = low ? z : nullptr;
     p.gate_w = low ? w : nullptr;
@@ -167,10 +172,13 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     const int algo = kda_prefill_resolved_algo(cfg, a->num_seqs);
     // the in-kernel low-rank gate runs on the matrix cores with bf16 factors (throughput
     // variant) or on the VALU (recurrent kernel); the pipelined variant does not have it
-    if (cfg->gate == KDA_GATE_LOWRANK &&
+    if (lowrank_gate(cfg) &&
         (algo == KDA_ALGO_CHUNKED_LATENCY || (algo == KDA_ALGO_CHUNKED_THROUGHPUT && cfg->io_dtype != KDA_DTYPE_BF16)))
         return KDA_ERR_UNSUPPORTED;
-    if (cfg->gate == KDA_GATE_HEAD && algo == KDA_ALGO_CHUNKED_LATENCY) return KDA_ERR_UNSUPPORTED;
+    // the pipelined variant has neither the head gate nor the per-token path for decays
+    // without a floor
+    if ((cfg->gate == KDA_GATE_HEAD || cfg->gate == KDA_GATE_LOG_ALPHA_UNBOUNDED) && algo == KDA_ALGO_CHUNKED_LATENCY)
+        return KDA_ERR_UNSUPPORTED;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     int32_t *order = need > 0 ? static_cast<int32_t *>(a->workspace) : nullptr;

@@ -142,6 +142,17 @@ __device__ __forceinline__ float half_wave_sum(float x) {
     return x;
 }
 
+// Sum over the four 16-lane rows of the wave (lanes l, l ^ 16, l ^ 32, l ^ 48), with the
+// gfx950 row swaps: permlane16_swap exchanges rows 1 <-> 0 and 3 <-> 2 between its two
+// operands, permlane32_swap the upper half of one with the lower half of the other, so
+// that the two results of each add up to the xor-16 and then the xor-32 butterfly.
+__device__ __forceinline__ float row_group_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
 #pragma unroll

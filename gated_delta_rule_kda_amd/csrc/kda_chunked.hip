@@ -22,7 +22,11 @@
 // e^{G_s} e^{-G_j} within the chunk; at the log-decay floor of -5 per token
 // ("Kimi K3's Architecture ...", section "Channel-wise decay, and the floor
 // K3 puts under it") a 16-token chunk keeps e^{-G} <= e^80, inside the fp32 /
-// bf16 exponent range.
+// bf16 exponent range.  Without the floor (Kimi Linear's unbounded gate, same
+// section) a channel can decay further within one chunk; such a chunk is found
+// by a vote over the channels' chunk totals and takes the per-token recurrence
+// instead, in fp32 on the vector units, with the state in the same registers
+// (the position-pair fallback of that section, taken only where it is needed).
 //
 // Work layout: one workgroup of 8 waves per (sequence, head), walking the
 // sequence's chunks; about 80 KB of LDS and at most 128 VGPRs, so two
@@ -95,6 +99,20 @@ constexpr int ZPK = 128 + 8;
 constexpr int OFF_ZL = LDS_BYTES;
 constexpr int LDS_BYTES_LOWRANK = OFF_ZL + C * ZPK * 2;
 
+// Per-token path of a chunk whose decay leaves the factorised range: fp32 k^ and q^ rows
+// [16][FPK] in the K / Q planes; alpha [16][128] in the k^ / Gamma plane, written with the
+// running sums (that plane is free from the first barrier of a chunk until the operands
+// are built); the V rows, which each token's outputs overwrite once they are read.  The
+// vote flag shares the head-gate slot.
+constexpr int OFF_KF = OFF_KL;
+constexpr int OFF_QF = OFF_KF + C * FPK * 4;
+constexpr int OFF_AL = OFF_KRD;
+constexpr int OFF_FLAG = OFF_GH;
+// a chunk keeps the factorised path while every channel's decay over it stays above
+// 2^-WIDE_LOG2: e^{-G} <= 2^116 then, and the lo parts of e^{G} k^ stay normal in bf16
+constexpr float WIDE_LOG2 = 116.0f;
+static_assert(OFF_QF + C * FPK * 4 <= OFF_KHT, "fp32 k^ and q^ rows must fit in the K / Q planes");
+static_assert(C * D * 4 <= 2 * PL_CD * 2, "alpha must fit in the k^ / Gamma plane");
 static_assert(C * RAW_ROW <= OFF_KRD - OFF_CUR, "staged rows must fit under the K / Q / Khat planes");
 static_assert(C * FPK * 4 <= 2 * PL_CD * 2, "output staging must fit in the KRD slot");
 static_assert(2 * LDS_BYTES_LOWRANK <= 160 * 1024, "two workgroups per gfx950 CU");
@@ -105,16 +123,20 @@ constexpr float LOG2E = 1.4426950408889634f;
 // The second bound is waves per SIMD: two workgroups of 8 waves per CU need four
 // (at most 128 VGPRs).
 // GATE (KDA_GATE_*): log alpha read per channel, formed in the kernel from the low-rank
-// gate factors (bf16 io), or read as one value per (token, head).
-template <typename IO, typename OUT, int GATE>
+// gate factors (bf16 io; K3's floored sigmoid or Kimi Linear's softplus), or read as one
+// value per (token, head).  WIDE: chunks whose decay leaves the factorised range take the
+// per-token path (decays without a floor).
+template <typename IO, typename OUT, int GATE, bool WIDE>
 __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
-    constexpr bool LOWRANK = GATE == KDA_GATE_LOWRANK;
+    constexpr bool SOFTPLUS = GATE == KDA_GATE_LOWRANK_SOFTPLUS;
+    constexpr bool LOWRANK = GATE == KDA_GATE_LOWRANK || SOFTPLUS;
     // One decay per (token, head): Gamma is a row scale of the chunk's tokens, so it leaves
     // the channel contractions.  The operand planes hold k^ and q^ unscaled (the k^ plane
     // also serves as the Gram's B operand and, transposed, as Khat^T), and the factors are
     // applied to the 16 x 16 Gram tiles and to the rows of the products: X = V - Diag(Gamma)
     // (K^ S), O1 = Diag(Gamma) (Q^ S), S <- Gamma_C S + K^T (Diag(e^{G_C - G}) U).
     constexpr bool HEADG = GATE == KDA_GATE_HEAD;
+    static_assert(!(HEADG && WIDE), "the head gate's factors never exceed 1");
     using IV = Vec8<IO>;   // eight-wide rows of the conv cache
     using I4 = Vec4<IO>;
     using IB = BufLoad4<IO>;
@@ -136,6 +158,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     float *const RW = reinterpret_cast<float *>(smem + OFF_RW);
     float *const GH = reinterpret_cast<float *>(smem + OFF_GH);  // head gate only
     uint16_t *const ZL = reinterpret_cast<uint16_t *>(smem + OFF_ZL);  // LOWRANK only
+    float *const KF = reinterpret_cast<float *>(smem + OFF_KF);          // per-token path only
+    float *const QF = reinterpret_cast<float *>(smem + OFF_QF);
+    float *const AL = reinterpret_cast<float *>(smem + OFF_AL);
+    int *const FLAG = reinterpret_cast<int *>(smem + OFF_FLAG);
 
     const int H = p.H;
     const int item = blockIdx.x;
@@ -174,9 +200,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     }
     if (tid < D) RW[tid] = p.rms_w ? p.rms_w[tid] : 1.0f;
     const float l2_eps = p.l2_eps * (LOG2E * LOG2E);
-    // low-rank gate: this lane's channel bias and e^{A_h} log2(e)
+    // low-rank gate: this lane's channel bias and e^{A_h} log2(e) (inside the sigmoid), or
+    // e^{A_h} (outside the softplus, which works in log2 units)
     const float gbias = LOWRANK ? p.gate_bias[hD + col] : 0.0f;
-    const float gscale = LOWRANK ? __expf(p.gate_a[h]) * LOG2E : 0.0f;
+    const float gscale = LOWRANK ? __expf(p.gate_a[h]) * (SOFTPLUS ? 1.0f : LOG2E) : 0.0f;
 
     // ---- state slice in accumulator layout: S[t][i] = S(16t + 4lh + i, col) ----------------
     const int row_in = p.slots_in ? p.slots_in[n] : n;     // state_in / conv_in row
@@ -313,6 +340,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             store4f(LA + et * D + ec0, la);
         }
         if ((tid & 31) == 0) BETA[et] = bet;
+        if (WIDE && tid == 0) *FLAG = 0;
         if (LOWRANK) load_w();  // this lane's W_up operand, used right after the barrier
         __syncthreads();
 
@@ -332,9 +360,19 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             float acc_sum = 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float t = (zacc[i] + gbias) * gscale;  // e^{A_h} (z + b) log2(e)
-                const float la2 = (-5.0f * LOG2E) * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
-                acc_sum += r0 + 4 * lh + i < L ? la2 : 0.0f;
+                float la2;
+                if (SOFTPLUS) {
+                    // -e^{A_h} softplus(u) log2(e) = -e^{A_h} log2(1 + 2^t), t = u log2(e),
+                    // as max(t, 0) + log2(1 + 2^-|t|) so that 2^t never overflows
+                    const float t = (zacc[i] + gbias) * LOG2E;
+                    la2 = -gscale * (fmaxf(t, 0.0f) + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-fabsf(t))));
+                } else {
+                    const float t = (zacc[i] + gbias) * gscale;  // e^{A_h} (z + b) log2(e)
+                    la2 = (-5.0f * LOG2E) * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
+                }
+                la2 = r0 + 4 * lh + i < L ? la2 : 0.0f;
+                if (WIDE) AL[(4 * lh + i) * D + col] = __builtin_amdgcn_exp2f(la2);
+                acc_sum += la2;
                 run[i] = acc_sum;
             }
             const int lid = lane;
@@ -345,7 +383,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             const float before = x2 - acc_sum;  // sum over the rows of the earlier row groups
 #pragma unroll
             for (int i = 0; i < 4; ++i) LA[(4 * lh + i) * D + col] = run[i] + before;
-            if (lh == 3) EGC[col] = __builtin_amdgcn_exp2f(run[3] + before);
+            if (lh == 3) {
+                EGC[col] = __builtin_amdgcn_exp2f(run[3] + before);
+                if (WIDE && run[3] + before < -WIDE_LOG2) *FLAG = 1;
+            }
         }
         float xq[4], xk[4], xv[4];
         {
@@ -417,12 +458,18 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             float g = 0.0f;
 #pragma unroll
             for (int r = 0; r < C; ++r) {
-                g += LA[r * D + c];
+                const float x = LA[r * D + c];
+                if (WIDE) AL[r * D + c] = __builtin_amdgcn_exp2f(x);  // for the per-token path
+                g += x;
                 LA[r * D + c] = g;
             }
             EGC[c] = __builtin_amdgcn_exp2f(g);
+            if (WIDE && g < -WIDE_LOG2) *FLAG = 1;
         }
         __syncthreads();
+        // one channel decays past the factorised range within this chunk: the chunk takes
+        // the per-token path (the same value in every thread)
+        const bool wide = WIDE && *FLAG != 0;
 
         // ---- 3. staged operands (bf16 hi/lo); the next chunk's conv history ------------------
         if (et >= C - CONV_HIST) {
@@ -431,7 +478,12 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 #pragma unroll
             for (int s = 0; s < 3; ++s) store4f(raw_t + (s - 3 * C) * D, xr[s]);
         }
-        if (HEADG) {
+        if (wide) {
+            // fp32 k^, q^ and v (the per-token alpha is in place since the gate stage)
+            store4f(KF + et * FPK + ec0, xk);
+            store4f(QF + et * FPK + ec0, xq);
+            store4f(VB + et * FPK + ec0, xv);
+        } else if (HEADG) {
             // k^ and q^ unscaled; the k^ split also fills the transposed Khat^T plane
             const int at = et * OPK + cperm(ec0);
             uint2 hi, lo;
@@ -489,177 +541,232 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             store4f(VB + et * FPK + ec0, xv);
         }
         __syncthreads();
-        // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
-        if (wave < 2) {
-            // the Gram blocks and T gate the next barrier for the whole workgroup: their
-            // waves take issue priority over the other waves of their SIMDs meanwhile
-            __builtin_amdgcn_s_setprio(2);
-            const uint16_t *Lh = wave == 0 ? KLh : QLh;
-            // two independent accumulation chains (channels 0-63 and 64-127) halve the
-            // dependent-MFMA latency on this critical path
-            f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        if (wide) {
+            // ---- 4-5, per-token path: for each token u of the chunk in order,
+            //   S <- Diag(alpha_u) S;  r = S^T k_u;  du = beta_u (v_u - r);
+            //   S <- S + k_u du^T;     o~_u = S^T q_u   (q carries the read scale)
+            // in two passes over the lane's rows, each ending in one column sum over the four
+            // row groups.  Lane (lh, ln) of wave w holds rows 16t + 4lh + i of column
+            // 16w + ln; each row step waits for its own two operand loads (with more of them
+            // in flight the loop needs registers that the matrix-core path then spills).
+            // The lane offsets are rebuilt from an opaque thread index rather than kept live.
+            const int x = opaque(tid);
+            const int lrow = 4 * ((x & 63) >> 4), lcol = ((x >> 6) << 4) + (x & 15);
+            for (int u = 0; u < rend - r0; ++u) {
+                const float *const al = AL + u * D + lrow;
+                const float *const kf = KF + u * FPK + lrow;
+                const float *const qf = QF + u * FPK + lrow;
+                float r4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) {
-                const int ka = ln * OPK + 32 * s + 8 * lh;
-                const uint4 ah = *reinterpret_cast<const uint4 *>(Lh + ka);
-                const uint4 al = *reinterpret_cast<const uint4 *>(Lh + PL_CD + ka);
-                const uint16_t *Bp = HEADG ? KLh : KRDh;  // k^ / Gamma, or k^ for the head gate
-                const uint4 bh = *reinterpret_cast<const uint4 *>(Bp + ka);
-                const uint4 bl = *reinterpret_cast<const uint4 *>(Bp + PL_CD + ka);
-                acc2[s >> 1] = mma3(ah, al, bh, bl, acc2[s >> 1]);
-            }
-            f32x4_t acc = acc2[0] + acc2[1];
-            if (HEADG) {  // row s, column j of the Gram tile times e^{G_s - G_j} (<= 1 for j <= s)
-                const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
-                const float gj = GH[ln];
-                acc[0] *= __builtin_amdgcn_exp2f(fminf(gr.x - gj, 0.0f));
-                acc[1] *= __builtin_amdgcn_exp2f(fminf(gr.y - gj, 0.0f));
-                acc[2] *= __builtin_amdgcn_exp2f(fminf(gr.z - gj, 0.0f));
-                acc[3] *= __builtin_amdgcn_exp2f(fminf(gr.w - gj, 0.0f));
-            }
-            if (wave == 0) {
-                // T = (I + A)^{-1} Diag(beta) by forward substitution in fp32: lane 4j + r
-                // carries rows r, r+4, r+8, r+12 of column j of (I + A)^{-1}; step k
-                // broadcasts row k inside the quad and removes A[i][k] x_k from every row
-                // (A is strictly lower, so rows i <= k are left unchanged).  A goes through
-                // LDS k-major, AF[k][r][q] = A[4q + r][k], so that step k reads one float4.
-                {
-                    const float4 b4 = *reinterpret_cast<const float4 *>(BETA + 4 * lh);
-                    const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) AF[ln * AFK + 4 * i + lh] = ln < 4 * lh + i ? acc[i] * bv[i] : 0.0f;
+                for (int t = 0; t < 8; ++t) {
+                    const float4 a4 = *reinterpret_cast<const float4 *>(al + 16 * t);
+                    const float4 k4 = *reinterpret_cast<const float4 *>(kf + 16 * t);
+                    S[t][0] *= a4.x;
+                    S[t][1] *= a4.y;
+                    S[t][2] *= a4.z;
+                    S[t][3] *= a4.w;
+                    r4[0] = fmaf(S[t][0], k4.x, r4[0]);
+                    r4[1] = fmaf(S[t][1], k4.y, r4[1]);
+                    r4[2] = fmaf(S[t][2], k4.z, r4[2]);
+                    r4[3] = fmaf(S[t][3], k4.w, r4[3]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-                const int x = opaque(lane), j = x >> 2, r = x & 3;
-                float xv[4];
+                const float r = row_group_sum((r4[0] + r4[1]) + (r4[2] + r4[3]));
+                // v_u is read by the four lanes of this column (one wave) before the lane
+                // with lh = 0 overwrites its slot with the output row below
+                const float du = BETA[u] * (VB[u * FPK + lcol] - r);
+                float o4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) xv[q] = (4 * q + r == j) ? 1.0f : 0.0f;
+                for (int t = 0; t < 8; ++t) {
+                    const float4 k4 = *reinterpret_cast<const float4 *>(kf + 16 * t);
+                    const float4 q4 = *reinterpret_cast<const float4 *>(qf + 16 * t);
+                    S[t][0] = fmaf(k4.x, du, S[t][0]);
+                    S[t][1] = fmaf(k4.y, du, S[t][1]);
+                    S[t][2] = fmaf(k4.z, du, S[t][2]);
+                    S[t][3] = fmaf(k4.w, du, S[t][3]);
+                    o4[0] = fmaf(S[t][0], q4.x, o4[0]);
+                    o4[1] = fmaf(S[t][1], q4.y, o4[1]);
+                    o4[2] = fmaf(S[t][2], q4.z, o4[2]);
+                    o4[3] = fmaf(S[t][3], q4.w, o4[3]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                const float o = row_group_sum((o4[0] + o4[1]) + (o4[2] + o4[3]));
+                if (lrow == 0) VB[u * FPK + lcol] = o;
+            }
+            if (ch + 1 < nchunks) load_current(ch + 1);
+        } else {
+            // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
+            if (wave < 2) {
+                // the Gram blocks and T gate the next barrier for the whole workgroup: their
+                // waves take issue priority over the other waves of their SIMDs meanwhile
+                __builtin_amdgcn_s_setprio(2);
+                const uint16_t *Lh = wave == 0 ? KLh : QLh;
+                // two independent accumulation chains (channels 0-63 and 64-127) halve the
+                // dependent-MFMA latency on this critical path
+                f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-                for (int k = 0; k < C; ++k) {
-                    float xk;
-                    switch (k & 3) {  // x_k, from lane 4j + k % 4 of the quad
-                        case 0: xk = dpp<0x00>(xv[k >> 2]); break;
-                        case 1: xk = dpp<0x55>(xv[k >> 2]); break;
-                        case 2: xk = dpp<0xAA>(xv[k >> 2]); break;
-                        default: xk = dpp<0xFF>(xv[k >> 2]); break;
+                for (int s = 0; s < D / 32; ++s) {
+                    const int ka = ln * OPK + 32 * s + 8 * lh;
+                    const uint4 ah = *reinterpret_cast<const uint4 *>(Lh + ka);
+                    const uint4 al = *reinterpret_cast<const uint4 *>(Lh + PL_CD + ka);
+                    const uint16_t *Bp = HEADG ? KLh : KRDh;  // k^ / Gamma, or k^ for the head gate
+                    const uint4 bh = *reinterpret_cast<const uint4 *>(Bp + ka);
+                    const uint4 bl = *reinterpret_cast<const uint4 *>(Bp + PL_CD + ka);
+                    acc2[s >> 1] = mma3(ah, al, bh, bl, acc2[s >> 1]);
+                }
+                f32x4_t acc = acc2[0] + acc2[1];
+                if (HEADG) {  // row s, column j of the Gram tile times e^{G_s - G_j} (<= 1 for j <= s)
+                    const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
+                    const float gj = GH[ln];
+                    acc[0] *= __builtin_amdgcn_exp2f(fminf(gr.x - gj, 0.0f));
+                    acc[1] *= __builtin_amdgcn_exp2f(fminf(gr.y - gj, 0.0f));
+                    acc[2] *= __builtin_amdgcn_exp2f(fminf(gr.z - gj, 0.0f));
+                    acc[3] *= __builtin_amdgcn_exp2f(fminf(gr.w - gj, 0.0f));
+                }
+                if (wave == 0) {
+                    // T = (I + A)^{-1} Diag(beta) by forward substitution in fp32: lane 4j + r
+                    // carries rows r, r+4, r+8, r+12 of column j of (I + A)^{-1}; step k
+                    // broadcasts row k inside the quad and removes A[i][k] x_k from every row
+                    // (A is strictly lower, so rows i <= k are left unchanged).  A goes through
+                    // LDS k-major, AF[k][r][q] = A[4q + r][k], so that step k reads one float4.
+                    {
+                        const float4 b4 = *reinterpret_cast<const float4 *>(BETA + 4 * lh);
+                        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) AF[ln * AFK + 4 * i + lh] = ln < 4 * lh + i ? acc[i] * bv[i] : 0.0f;
                     }
-                    const float4 a = *reinterpret_cast<const float4 *>(AF + k * AFK + 4 * r);
-                    xv[0] = fmaf(-a.x, xk, xv[0]);
-                    xv[1] = fmaf(-a.y, xk, xv[1]);
-                    xv[2] = fmaf(-a.z, xk, xv[2]);
-                    xv[3] = fmaf(-a.w, xk, xv[3]);
-                }
-                const float bj = BETA[j];
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                    const int x = opaque(lane), j = x >> 2, r = x & 3;
+                    float xv[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint16_t sh, sl;
-                    split1(xv[q] * bj, sh, sl);
-                    TMh[(4 * q + r) * OPT + j] = sh;
-                    TMh[PL_CC + (4 * q + r) * OPT + j] = sl;
+                    for (int q = 0; q < 4; ++q) xv[q] = (4 * q + r == j) ? 1.0f : 0.0f;
+#pragma unroll
+                    for (int k = 0; k < C; ++k) {
+                        float xk;
+                        switch (k & 3) {  // x_k, from lane 4j + k % 4 of the quad
+                            case 0: xk = dpp<0x00>(xv[k >> 2]); break;
+                            case 1: xk = dpp<0x55>(xv[k >> 2]); break;
+                            case 2: xk = dpp<0xAA>(xv[k >> 2]); break;
+                            default: xk = dpp<0xFF>(xv[k >> 2]); break;
+                        }
+                        const float4 a = *reinterpret_cast<const float4 *>(AF + k * AFK + 4 * r);
+                        xv[0] = fmaf(-a.x, xk, xv[0]);
+                        xv[1] = fmaf(-a.y, xk, xv[1]);
+                        xv[2] = fmaf(-a.z, xk, xv[2]);
+                        xv[3] = fmaf(-a.w, xk, xv[3]);
+                    }
+                    const float bj = BETA[j];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint16_t sh, sl;
+                        split1(xv[q] * bj, sh, sl);
+                        TMh[(4 * q + r) * OPT + j] = sh;
+                        TMh[PL_CC + (4 * q + r) * OPT + j] = sl;
+                    }
+                } else {
+                    const int j = ln;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * lh + i;
+                        uint16_t sh, sl;
+                        split1(j <= r ? acc[i] : 0.0f, sh, sl);
+                        PMh[r * OPT + j] = sh;
+                        PMh[PL_CC + r * OPT + j] = sl;
+                    }
                 }
-            } else {
-                const int j = ln;
+                __builtin_amdgcn_s_setprio(0);
+            }
+            // X = V - Kbar S0 and O1 = Qbar S0.  S0 is the B operand: K step s holds rows
+            // 32s + pi(slot), split into bf16 hi/lo right before use.
+            f32x4_t X = {0.f, 0.f, 0.f, 0.f}, O1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int ka = ln * OPK + 32 * s + 8 * lh;
+                const uint4 kh = *reinterpret_cast<const uint4 *>(KLh + ka);
+                const uint4 kl_ = *reinterpret_cast<const uint4 *>(KLh + PL_CD + ka);
+                const uint4 qh = *reinterpret_cast<const uint4 *>(QLh + ka);
+                const uint4 ql_ = *reinterpret_cast<const uint4 *>(QLh + PL_CD + ka);
+                const float v8[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
+                                     S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
+                uint4 sh, sl;
+                split8(v8, sh, sl);
+                X = mma3(kh, kl_, sh, sl, X);
+                O1 = mma3(qh, ql_, sh, sl, O1);
+            }
+            if (HEADG) {  // the row scales Gamma of Kbar = Diag(Gamma) K^ and Qbar = Diag(Gamma) Q^
+                const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
+                const float e4[4] = {__builtin_amdgcn_exp2f(gr.x), __builtin_amdgcn_exp2f(gr.y),
+                                     __builtin_amdgcn_exp2f(gr.z), __builtin_amdgcn_exp2f(gr.w)};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 4 * lh + i;
-                    uint16_t sh, sl;
-                    split1(j <= r ? acc[i] : 0.0f, sh, sl);
-                    PMh[r * OPT + j] = sh;
-                    PMh[PL_CC + r * OPT + j] = sl;
+                    X[i] *= e4[i];
+                    O1[i] *= e4[i];
                 }
             }
-            __builtin_amdgcn_s_setprio(0);
-        }
-        // X = V - Kbar S0 and O1 = Qbar S0.  S0 is the B operand: K step s holds rows
-        // 32s + pi(slot), split into bf16 hi/lo right before use.
-        f32x4_t X = {0.f, 0.f, 0.f, 0.f}, O1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int ka = ln * OPK + 32 * s + 8 * lh;
-            const uint4 kh = *reinterpret_cast<const uint4 *>(KLh + ka);
-            const uint4 kl_ = *reinterpret_cast<const uint4 *>(KLh + PL_CD + ka);
-            const uint4 qh = *reinterpret_cast<const uint4 *>(QLh + ka);
-            const uint4 ql_ = *reinterpret_cast<const uint4 *>(QLh + PL_CD + ka);
-            const float v8[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
-                                 S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
-            uint4 sh, sl;
-            split8(v8, sh, sl);
-            X = mma3(kh, kl_, sh, sl, X);
-            O1 = mma3(qh, ql_, sh, sl, O1);
-        }
-        if (HEADG) {  // the row scales Gamma of Kbar = Diag(Gamma) K^ and Qbar = Diag(Gamma) Q^
-            const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
-            const float e4[4] = {__builtin_amdgcn_exp2f(gr.x), __builtin_amdgcn_exp2f(gr.y),
-                                 __builtin_amdgcn_exp2f(gr.z), __builtin_amdgcn_exp2f(gr.w)};
+            for (int i = 0; i < 4; ++i) X[i] = VB[(4 * lh + i) * FPK + col] - X[i];
+            const Split4 Xs(X);
+            // S has been read: decay it now, S <- Diag(Gamma_C) S, in the time the Gram / T
+            // waves need before the barrier (they decay theirs after it)
+            const bool late_decay = wave == 0;
+            auto decay = [&]() {
+                if (HEADG) {
+                    const float g = GH[C];  // e^{G_C}, one factor for the whole state
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                X[i] *= e4[i];
-                O1[i] *= e4[i];
-            }
-        }
+                    for (int t = 0; t < 8; ++t) S[t] *= g;
+                    return;
+                }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) X[i] = VB[(4 * lh + i) * FPK + col] - X[i];
-        const Split4 Xs(X);
-        // S has been read: decay it now, S <- Diag(Gamma_C) S, in the time the Gram / T
-        // waves need before the barrier (they decay theirs after it)
-        const bool late_decay = wave == 0;
-        auto decay = [&]() {
-            if (HEADG) {
-                const float g = GH[C];  // e^{G_C}, one factor for the whole state
-#pragma unroll
-                for (int t = 0; t < 8; ++t) S[t] *= g;
-                return;
-            }
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float4 g4 = *reinterpret_cast<const float4 *>(EGC + 16 * t + 4 * lh);
-                S[t][0] *= g4.x;
-                S[t][1] *= g4.y;
-                S[t][2] *= g4.z;
-                S[t][3] *= g4.w;
-            }
-        };
-        if (!late_decay) decay();
-        __syncthreads();
+                for (int t = 0; t < 8; ++t) {
+                    const float4 g4 = *reinterpret_cast<const float4 *>(EGC + 16 * t + 4 * lh);
+                    S[t][0] *= g4.x;
+                    S[t][1] *= g4.y;
+                    S[t][2] *= g4.z;
+                    S[t][3] *= g4.w;
+                }
+            };
+            if (!late_decay) decay();
+            __syncthreads();
 
-        // ---- 5. U = T X, O = scale (Qbar S + P U), S <- Diag(Gamma_C) S + Khat^T U -------------
-        if (ch + 1 < nchunks) load_current(ch + 1);
-        {
-            const uint2 Th = *reinterpret_cast<const uint2 *>(TMh + ln * OPT + 4 * lh);
-            const uint2 Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh);
-            const uint2 Ph = *reinterpret_cast<const uint2 *>(PMh + ln * OPT + 4 * lh);
-            const uint2 Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + ln * OPT + 4 * lh);
-            const f32x4_t Uf = mma16x2(Th, Tl, Xs.h, Xs.l, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            const Split4 Us(Uf);
-            const f32x4_t O = mma16x2(Ph, Pl, Us.h, Us.l, O1);  // Qbar S + P U
+            // ---- 5. U = T X, O = scale (Qbar S + P U), S <- Diag(Gamma_C) S + Khat^T U -------------
+            if (ch + 1 < nchunks) load_current(ch + 1);
+            {
+                const uint2 Th = *reinterpret_cast<const uint2 *>(TMh + ln * OPT + 4 * lh);
+                const uint2 Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh);
+                const uint2 Ph = *reinterpret_cast<const uint2 *>(PMh + ln * OPT + 4 * lh);
+                const uint2 Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + ln * OPT + 4 * lh);
+                const f32x4_t Uf = mma16x2(Th, Tl, Xs.h, Xs.l, f32x4_t{0.f, 0.f, 0.f, 0.f});
+                const Split4 Us(Uf);
+                const f32x4_t O = mma16x2(Ph, Pl, Us.h, Us.l, O1);  // Qbar S + P U
 #pragma unroll
-            for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = O[i];
-            if (late_decay) decay();
-            // Khat^T U with the products split as in mma16x2.  Rows of odd tiles hold their
-            // two token pairs swapped (the plane's bank swizzle), so those tiles take the
-            // U operand with its pairs swapped to match.
-            Split4 Uk = Us;
-            if (HEADG) {  // Khat^T U = K^T (Diag(e^{G_C - G}) U): scale the rows of U
-                const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
-                const float gc = GH[C - 1];
-                const float u4[4] = {Uf[0] * __builtin_amdgcn_exp2f(gc - gr.x), Uf[1] * __builtin_amdgcn_exp2f(gc - gr.y),
-                                     Uf[2] * __builtin_amdgcn_exp2f(gc - gr.z), Uf[3] * __builtin_amdgcn_exp2f(gc - gr.w)};
-                Uk = Split4(u4);
-            }
-            const uint4 ub_e = make_uint4(Uk.h.x, Uk.h.y, Uk.h.x, Uk.h.y), ul_e = make_uint4(Uk.l.x, Uk.l.y, 0u, 0u);
-            const uint4 ub_o = make_uint4(Uk.h.y, Uk.h.x, Uk.h.y, Uk.h.x), ul_o = make_uint4(Uk.l.y, Uk.l.x, 0u, 0u);
+                for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = O[i];
+                if (late_decay) decay();
+                // Khat^T U with the products split as in mma16x2.  Rows of odd tiles hold their
+                // two token pairs swapped (the plane's bank swizzle), so those tiles take the
+                // U operand with its pairs swapped to match.
+                Split4 Uk = Us;
+                if (HEADG) {  // Khat^T U = K^T (Diag(e^{G_C - G}) U): scale the rows of U
+                    const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
+                    const float gc = GH[C - 1];
+                    const float u4[4] = {Uf[0] * __builtin_amdgcn_exp2f(gc - gr.x), Uf[1] * __builtin_amdgcn_exp2f(gc - gr.y),
+                                         Uf[2] * __builtin_amdgcn_exp2f(gc - gr.z), Uf[3] * __builtin_amdgcn_exp2f(gc - gr.w)};
+                    Uk = Split4(u4);
+                }
+                const uint4 ub_e = make_uint4(Uk.h.x, Uk.h.y, Uk.h.x, Uk.h.y), ul_e = make_uint4(Uk.l.x, Uk.l.y, 0u, 0u);
+                const uint4 ub_o = make_uint4(Uk.h.y, Uk.h.x, Uk.h.y, Uk.h.x), ul_o = make_uint4(Uk.l.y, Uk.l.x, 0u, 0u);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int c = 16 * t + ln;
-                // tokens 4lh .. 4lh+3 of row c sit at group lh ^ (t / 2)
-                const int ka = c * KHTR + 4 * (lh ^ (t >> 1));
-                const uint2 ah = *reinterpret_cast<const uint2 *>(KHTh + ka);
-                const uint2 al = *reinterpret_cast<const uint2 *>(KHTh + C + ka);
-                const uint4 a = make_uint4(ah.x, ah.y, al.x, al.y);
-                S[t] = mma(a, (t & 1) ? ub_o : ub_e, S[t]);
-                S[t] = mma(a, (t & 1) ? ul_o : ul_e, S[t]);
+                for (int t = 0; t < 8; ++t) {
+                    const int c = 16 * t + ln;
+                    // tokens 4lh .. 4lh+3 of row c sit at group lh ^ (t / 2)
+                    const int ka = c * KHTR + 4 * (lh ^ (t >> 1));
+                    const uint2 ah = *reinterpret_cast<const uint2 *>(KHTh + ka);
+                    const uint2 al = *reinterpret_cast<const uint2 *>(KHTh + C + ka);
+                    const uint4 a = make_uint4(ah.x, ah.y, al.x, al.y);
+                    S[t] = mma(a, (t & 1) ? ub_o : ub_e, S[t]);
+                    S[t] = mma(a, (t & 1) ? ul_o : ul_e, S[t]);
+                }
             }
         }
         __syncthreads();
@@ -667,7 +774,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         // ---- 6. epilogue: sigma(g) * RMSNorm(o~) * w ------------------------------------------
         {
             float o[4];
-            load4f(OB + et * FPK + ec0, o);
+            load4f((wide ? VB : OB) + et * FPK + ec0, o);
             if (p.epilogue) {
                 float ss = 0.f;
 #pragma unroll
@@ -727,24 +834,35 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 template <typename IO, typename OUT>
 hipError_t launch(const LayerParams &p, hipStream_t s) {
     if (p.num_items == 0) return hipSuccess;
+    // log alpha with the floor of -5 never leaves the factorised range; without a floor the
+    // chunks past it are found by the vote and take the per-token path
     if (p.gate == KDA_GATE_HEAD)
-        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_HEAD>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_HEAD, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+    else if (p.gate == KDA_GATE_LOG_ALPHA_UNBOUNDED)
+        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_LOG_ALPHA, true>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     else
-        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_LOG_ALPHA>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_LOG_ALPHA, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename OUT>
 hipError_t launch_lowrank(const LayerParams &p, hipStream_t s) {
     if (p.num_items == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOWRANK>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+    // K3's gate stays above its floor of -5 per token, so its chunks never leave the
+    // factorised range; Kimi Linear's softplus gate has no floor
+    if (p.gate == KDA_GATE_LOWRANK_SOFTPLUS)
+        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOWRANK_SOFTPLUS, true>), dim3(p.num_items),
+                           dim3(THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOWRANK, false>), dim3(p.num_items), dim3(THREADS),
+                           0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_chunked_throughput(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s) {
-    if (p.gate == KDA_GATE_LOWRANK) {  // bf16 io only (checked by the caller)
+    if (p.gate == KDA_GATE_LOWRANK || p.gate == KDA_GATE_LOWRANK_SOFTPLUS) {  // bf16 io only (checked by the caller)
         if (io_dtype != KDA_DTYPE_BF16) return hipErrorInvalidValue;
         return out_dtype == KDA_DTYPE_BF16 ? launch_lowrank<uint16_t>(p, s) : launch_lowrank<float>(p, s);
     }

@@ -31,7 +31,8 @@ struct LayerParams {
     void *o;
     float scale, l2_eps, rms_eps;
     int32_t prologue, epilogue;
-    // KDA_GATE_LOWRANK: log alpha = -5 sigmoid(e^{A_h} (z W^T + b)) formed in the kernel
+    // KDA_GATE_LOWRANK: log alpha = -5 sigmoid(e^{A_h} (z W^T + b)) formed in the kernel;
+    // KDA_GATE_LOWRANK_SOFTPLUS: log alpha = -e^{A_h} softplus(z W^T + b)
     int32_t gate, gate_rank;
     const void *gate_z;          // [tokens][r] io dtype
     const void *gate_w;          // [H*128][r] io dtype

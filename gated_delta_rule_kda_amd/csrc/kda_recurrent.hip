@@ -42,7 +42,8 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 // log alpha of key channel c of head h at token t from the low-rank gate factors: an
-// fp32 dot product over the rank, then -5 sigmoid(e^{A_h} (z + b)).
+// fp32 dot product over the rank, then -5 sigmoid(e^{A_h} (z + b)), or for Kimi Linear's
+// gate -e^{A_h} softplus(z + b) = -e^{A_h} (max(u, 0) + log(1 + e^{-|u|})).
 template <typename IO>
 __device__ __forceinline__ float lowrank_log_alpha(const LayerParams &p, int64_t t, int h, int c, float e_a) {
     using IOT = IoTraits<IO>;
@@ -54,8 +55,9 @@ __device__ __forceinline__ float lowrank_log_alpha(const LayerParams &p, int64_t
         acc0 = fmaf(IOT::load(p.gate_z, zrow + j), IOT::load(p.gate_w, wrow + j), acc0);
         acc1 = fmaf(IOT::load(p.gate_z, zrow + j + 1), IOT::load(p.gate_w, wrow + j + 1), acc1);
     }
-    const float u = e_a * ((acc0 + acc1) + p.gate_bias[static_cast<size_t>(h) * D + c]);
-    return -5.0f * sigmoidf_(u);
+    const float u = (acc0 + acc1) + p.gate_bias[static_cast<size_t>(h) * D + c];
+    if (p.gate == KDA_GATE_LOWRANK_SOFTPLUS) return -e_a * (fmaxf(u, 0.0f) + log1pf(__expf(-fabsf(u))));
+    return -5.0f * sigmoidf_(e_a * u);
 }
 
 template <typename IO, typename OUT>

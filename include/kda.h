@@ -30,9 +30,10 @@
  *    io_dtype: the last three pre-conv inputs of each stream.  Conv weights
  *    are fp32 [3 streams][H*128][4]; tap j multiplies x_{t-j}; no bias.
  *  - log_alpha is fp32 and must lie in [-5, 0] (the log-decay floor of "The
- *    lower bound on decay is a hardware decision", "Inside Kimi K3"); beta is
- *    fp32 in [0, 1].  These are documented preconditions, not checked on the
- *    device: values outside them may produce inf/NaN in the chunked kernel.
+ *    lower bound on decay is a hardware decision", "Inside Kimi K3") unless the
+ *    gate is KDA_GATE_LOG_ALPHA_UNBOUNDED (any value <= 0); beta is fp32 in
+ *    [0, 1].  These are documented preconditions, not checked on the device:
+ *    values outside them may produce inf/NaN in the chunked kernels.
  *  - Pointers are device pointers unless marked "host".  Every device pointer
  *    must be 16-byte aligned.  The caller owns every buffer; the library
  *    allocates no device memory in these calls and keeps no pointer after it
@@ -93,6 +94,17 @@ typedef int32_t kda_status;
  * section "Channel-wise decay, and the floor K3 puts under it"): log_alpha is
  * [T][H].  A fast path: the decay factors leave the channel contractions. */
 #define KDA_GATE_HEAD 2
+/* LOWRANK_SOFTPLUS: Kimi Linear's gate, formed in the kernels from the same factors as
+ * LOWRANK: log alpha = -e^{A_h} softplus(z_down W_up^T + b), which has no floor
+ * ("Kimi K3's Architecture ...", section "Channel-wise decay, and the floor K3 puts
+ * under it").  Chunks in which some channel decays by more than 2^-116 take an exact
+ * per-token path in the chunked kernel; the others keep the matrix-core path. */
+#define KDA_GATE_LOWRANK_SOFTPLUS 3
+/* LOG_ALPHA_UNBOUNDED: log alpha passed as for LOG_ALPHA but with any value <= 0 (no
+ * floor, e.g. a Kimi Linear gate formed outside the library), handled as described for
+ * LOWRANK_SOFTPLUS.  On such chunks the per-token decay is taken from differences of
+ * running sums, whose fp32 rounding grows with the size of the sums. */
+#define KDA_GATE_LOG_ALPHA_UNBOUNDED 4
 
 typedef struct {
     int32_t num_heads;   /* H > 0 */
@@ -106,7 +118,7 @@ typedef struct {
     float l2_eps;        /* x / sqrt(sum x^2 + l2_eps) */
     float rms_eps;       /* x / sqrt(mean x^2 + rms_eps) */
     int32_t gate;        /* KDA_GATE_* */
-    int32_t gate_rank;   /* r of KDA_GATE_LOWRANK: a multiple of 32 in [32, 128] */
+    int32_t gate_rank;   /* r of the LOWRANK gates: a multiple of 32 in [32, 128] */
 } kda_config;
 
 /* Fills *cfg with the layer's defaults for H heads: bf16 io and output,
@@ -137,7 +149,8 @@ typedef struct {
     const int32_t *cu_seqlens;    /* device [N+1]: cu[0] = 0, non-decreasing, cu[N] = total_tokens */
     int64_t total_tokens;         /* T >= 0 */
     const void *q, *k, *v;        /* [T][H][128] io_dtype */
-    const float *log_alpha;       /* [T][H][128] fp32 in [-5, 0] (gate LOG_ALPHA), or [T][H] (gate HEAD); else unused */
+    const float *log_alpha;       /* [T][H][128] fp32 in [-5, 0] (gate LOG_ALPHA) or <= 0 (LOG_ALPHA_UNBOUNDED),
+                                     or [T][H] (gate HEAD); else unused */
     const float *beta;            /* [T][H] fp32, in [0, 1] */
     const void *g;                /* [T][H][128] io_dtype; required iff epilogue */
     const float *conv_w;          /* [3][H*128][4] fp32; required iff prologue */

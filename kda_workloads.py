@@ -261,6 +261,29 @@ def gen_gate(cu_seqlens, heads: int, rank: int = 128, seed: int = 1, io: str = "
     return {"gate_z": z[:, 0], "gate_w": w, "gate_bias": b, "gate_a": a}
 
 
+def gen_softplus_gate(cu_seqlens, heads: int, rank: int = 128, seed: int = 1, wild_heads=(),
+                      first_seq: int = 0) -> Dict[str, np.ndarray]:
+    """Factors of Kimi Linear's gate (log alpha = -e^A softplus(z_down W_up + b)), laid
+    out as gen_gate's.  z_down ~ N(0, 1) and W_up ~ N(0, 1/r) (bf16-rounded); A [H] is
+    the log of U(1, 16), one rate per head.  b_alpha: U(-7, -2.3) per channel, so that the
+    per-token decay is mostly small (softplus(b) ~ e^b in (1e-3, 0.1)); the heads listed in
+    wild_heads draw b ~ N(1, 1) instead, per-token log-decays of order -e^A (up to about
+    -30), which takes most of their 16-token chunks past e^-80 in some channel."""
+    cu = np.asarray(cu_seqlens, np.int64)
+    T = int(cu[-1])
+    z = np.zeros((T, 1, rank), np.float32)
+    _fill_blocks(z, seed, 22, cu, lambda rng, shape: _normal32(rng, shape), bf16=True,
+                 per_head=False, n0=first_seq)
+    rng = _rng(seed, 23)
+    w = _bf16_inplace((rng.standard_normal((heads * D, rank)) / np.sqrt(rank)).astype(np.float32))
+    a = np.log(rng.uniform(1.0, 16.0, heads)).astype(np.float32)
+    b = rng.uniform(-7.0, -2.3, heads * D)
+    wild = rng.normal(1.0, 1.0, heads * D)
+    for h in wild_heads:
+        b[h * D:(h + 1) * D] = wild[h * D:(h + 1) * D]
+    return {"gate_z": z[:, 0], "gate_w": w, "gate_bias": b.astype(np.float32), "gate_a": a}
+
+
 def varlen_lengths(n_seqs: int = 64, mean: float = 8192.0, sigma: float = 1.0,
                    lo: int = 16, hi: int = 65536, seed: int = 4) -> List[int]:
     """Lognormal lengths whose distribution mean is `mean` (mu = ln mean - sigma^2/2)."""

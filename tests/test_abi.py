@@ -204,3 +204,25 @@ def test_head_gate_arguments():
     one = dict(num_seqs=1, workspace=None, workspace_bytes=0)
     assert _prefill(kda.config(4, gate="head", algo="chunked_latency"), _args(**one)) == kda.ERR_UNSUPPORTED
     assert kda.resolved_algo(kda.config(4, gate="head"), 1) == "chunked_throughput"
+
+
+def test_unbounded_gate_arguments():
+    """Kimi Linear's softplus gate takes the low-rank factors like the K3 gate; log alpha
+    without a floor is required like log alpha; neither runs on the pipelined variant."""
+    low = dict(gate_z=FAKE, gate_w=FAKE, gate_bias=FAKE, gate_a=FAKE)
+    c = kda.config(4, gate="lowrank_softplus")
+    assert c.gate == 3
+    assert _prefill(c, _args(log_alpha=None, workspace=None, **low)) == kda.ERR_WORKSPACE_TOO_SMALL
+    assert _prefill(c, _args(log_alpha=None, gate_w=None, **{k: v for k, v in low.items() if k != "gate_w"})) \
+        == kda.ERR_INVALID_ARGUMENT
+    assert _prefill(kda.config(4, gate="lowrank_softplus", gate_rank=48), _args(**low)) == kda.ERR_UNSUPPORTED
+    u = kda.config(4, gate="log_alpha_unbounded")
+    assert u.gate == 4
+    assert _prefill(u, _args(log_alpha=None)) == kda.ERR_INVALID_ARGUMENT
+    assert _prefill(u, _args(workspace=None)) == kda.ERR_WORKSPACE_TOO_SMALL
+    one = dict(num_seqs=1, workspace=None, workspace_bytes=0)
+    for g in ("lowrank_softplus", "log_alpha_unbounded"):
+        assert _prefill(kda.config(4, gate=g, algo="chunked_latency"), _args(**one, **low)) == kda.ERR_UNSUPPORTED, g
+    bad = kda.config(4)
+    bad.gate = 5
+    assert _prefill(bad, _args()) == kda.ERR_INVALID_ARGUMENT

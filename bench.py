@@ -108,11 +108,18 @@ def load_traffic(path: str) -> dict:
 
 def run_extra_workloads(kda, W, dev, stream, log, algo="auto") -> dict:
     """Time the long-context (1 x 131072) and packed variable-length (64 sequences)
-    prefills: inputs generated one sequence at a time straight into device buffers."""
+    prefills, and the long context at 12 heads (one GPU's share of 96 heads split eight
+    ways): inputs generated one sequence at a time straight into device buffers.  The
+    long contexts are also timed in one sequential pass (the throughput variant) next to
+    AUTO's choice (the segmented prefill)."""
+    import dataclasses
     import torch
     out = {}
-    for name in ("prefill_131072", "varlen_64"):
-        spec = W.workload(name)
+    long12 = dataclasses.replace(W.workload("prefill_131072"), heads=12, name="prefill_131072_h12")
+    cases = [("prefill_131072", W.workload("prefill_131072"), [algo, "chunked_throughput"]),
+             ("prefill_131072_h12", long12, [algo, "chunked_throughput"]),
+             ("varlen_64", W.workload("varlen_64"), [algo])]
+    for name, spec, algos in cases:
         lens = [int(x) for x in spec.lens]
         N, H, T = len(lens), spec.heads, int(sum(lens))
         bf = torch.bfloat16
@@ -136,25 +143,29 @@ def run_extra_workloads(kda, W, dev, stream, log, algo="auto") -> dict:
         log(f"{name}: generated {T} tokens in {time.perf_counter() - t0:.1f}s")
         cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
         cwd = torch.from_numpy(cw).to(dev)
-        cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", prologue=True, epilogue=True, algo=algo)
         o = torch.empty((T, H, D), dtype=bf, device=dev)
         s_out = torch.empty_like(s0)
-        ws_n = kda.workspace_size(cfg, N, T)
-        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+        for a in algos:
+            cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", prologue=True, epilogue=True, algo=a)
+            ws_n = kda.workspace_size(cfg, N, T)
+            ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
-        def run():
-            kda.prefill(bufs["q"], bufs["k"], bufs["v"], la, beta, cu, g=bufs["g"], conv_w=cwd,
-                        state_in=s0, o=o, state_out=s_out, workspace=ws if ws_n else None, cfg=cfg,
-                        stream=stream, return_conv=False)
+            def run():
+                kda.prefill(bufs["q"], bufs["k"], bufs["v"], la, beta, cu, g=bufs["g"], conv_w=cwd,
+                            state_in=s0, o=o, state_out=s_out, workspace=ws if ws_n else None, cfg=cfg,
+                            stream=stream, return_conv=False)
 
-        run()
-        torch.cuda.synchronize()
-        ms, med = time_events(run, 3, stream)
-        nb = prefill_algorithmic_bytes(T, H, N) + N * H * D * D * 4  # + the initial states read
-        out[name] = {"tokens": T, "sequences": N, "max_len": max(lens), "ms": ms,
-                     "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nb,
-                     "frac_of_hbm_roofline": nb / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}
-        log(f"{name}: {ms:.2f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+            run()
+            torch.cuda.synchronize()
+            ms, med = time_events(run, 3, stream)
+            nb = prefill_algorithmic_bytes(T, H, N) + N * H * D * D * 4  # + the initial states read
+            key = name if a == algos[0] else f"{name}_{a}"
+            ran = kda.resolved_algo(cfg, N, T)
+            out[key] = {"tokens": T, "sequences": N, "heads": H, "max_len": max(lens), "algo": ran, "ms": ms,
+                        "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nb,
+                        "frac_of_hbm_roofline": nb / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}
+            log(f"{key} ({ran}): {ms:.2f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+            del ws
         del bufs, la, beta, s0, o, s_out
         torch.cuda.empty_cache()
     return out

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 HEAD_DIM = 128
 F32, BF16 = 0, 1
-ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2, "chunked_throughput": 3, "chunked_latency": 4}
+ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2, "chunked_throughput": 3, "chunked_latency": 4,
+         "chunked_scan": 5}
 GATES = {"log_alpha": 0, "lowrank": 1, "head": 2, "lowrank_softplus": 3, "log_alpha_unbounded": 4}
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 
@@ -69,6 +70,19 @@ class DecodeArgs(ctypes.Structure):
 _lib: Optional[ctypes.CDLL] = None
 
 
+def _init_device_runtime() -> None:
+    """Initialise the HIP runtime (through torch, which shares it with this library) before
+    the library registers its kernels: loading the library into an uninitialised runtime
+    after worker threads have started has left every later launch failing with
+    hipErrorNoDevice.  Nothing happens without a GPU."""
+    try:
+        import torch
+    except ImportError:
+        return
+    if torch.cuda.is_available():
+        torch.cuda.init()
+
+
 def lib() -> ctypes.CDLL:
     """Load the in-tree libkda.so (raises when it has not been built)."""
     global _lib
@@ -76,6 +90,7 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing; build it with "
                                "`python -m gated_delta_rule_kda_amd._build`")
+        _init_device_runtime()
         L = ctypes.CDLL(LIB_PATH)
         L.kda_config_init.argtypes = [ctypes.POINTER(Config), ctypes.c_int32]
         L.kda_config_init.restype = None
@@ -84,7 +99,7 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill_workspace_size.restype = ctypes.c_int32
         L.kda_prefill.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(PrefillArgs), _vp]
         L.kda_prefill.restype = ctypes.c_int32
-        L.kda_prefill_resolved_algo.argtypes = [ctypes.POINTER(Config), ctypes.c_int32]
+        L.kda_prefill_resolved_algo.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_int64]
         L.kda_prefill_resolved_algo.restype = ctypes.c_int32
         L.kda_decode_step.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(DecodeArgs), _vp]
         L.kda_decode_step.restype = ctypes.c_int32
@@ -302,10 +317,10 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
     return o
 
 
-def resolved_algo(cfg: Config, num_seqs: int = 1) -> str:
-    """Name of the prefill algorithm the library runs for `cfg` and `num_seqs` sequences
-    on the current device (AUTO and CHUNKED resolved)."""
-    code = lib().kda_prefill_resolved_algo(ctypes.byref(cfg), num_seqs)
+def resolved_algo(cfg: Config, num_seqs: int = 1, total_tokens: int = 0) -> str:
+    """Name of the prefill algorithm the library runs for `cfg`, `num_seqs` sequences and
+    `total_tokens` tokens on the current device (AUTO and CHUNKED resolved)."""
+    code = lib().kda_prefill_resolved_algo(ctypes.byref(cfg), num_seqs, total_tokens)
     if code < 0:
         raise KdaError(ERR_INVALID_ARGUMENT, "invalid configuration")
     return {v: k for k, v in ALGOS.items()}[code]

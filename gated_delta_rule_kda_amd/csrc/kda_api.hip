@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(256) void order_kernel(const int32_t *cu, int32_t n
     order[rank] = i;
 }
 
-bool valid_algo(int32_t a) { return a >= KDA_ALGO_AUTO && a <= KDA_ALGO_CHUNKED_LATENCY; }
+bool valid_algo(int32_t a) { return a >= KDA_ALGO_AUTO && a <= KDA_ALGO_CHUNKED_SCAN; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -96,6 +98,57 @@ void set_gate(LayerParams &p, const kda_config *cfg, const float *log_alpha, con
     p.gate_a = low ? a : nullptr;
 }
 
+// Compute units the segment plan assumes: a whole MI355X (gfx950) has 256.  The plan is
+// made without a HIP call, so that the host-only sizing and resolution functions never
+// initialise the runtime (and give the same answer on a host without a GPU); with fewer
+// compute units (a partitioned GPU) it is still correct, only split more finely.
+constexpr int PLAN_CUS = 256;
+int device_cu_count() { return PLAN_CUS; }
+
+// The segmented prefill takes bf16 io and the gates whose chunks never leave the
+// factorised range (the per-token path is not built into its kernel).
+bool scan_supported(const kda_config *cfg) {
+    return cfg->io_dtype == KDA_DTYPE_BF16 &&
+           (cfg->gate == KDA_GATE_LOG_ALPHA || cfg->gate == KDA_GATE_LOWRANK || cfg->gate == KDA_GATE_HEAD);
+}
+
+// Segment length (tokens, a multiple of the 16-token chunk) and table slots of the
+// segmented prefill: about two segments per compute unit over the N x H items, at
+// least 2048 tokens per segment when the choice is AUTO's (64 when asked for by name).
+struct ScanPlan {
+    int32_t seg_tokens, slots;
+};
+ScanPlan scan_plan(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens, bool named) {
+    const int64_t items = static_cast<int64_t>(num_seqs) * cfg->num_heads;
+    const int64_t per_seq = std::max<int64_t>(2, 2 * device_cu_count() / std::max<int64_t>(items, 1));
+    const int64_t avg = (total_tokens + num_seqs - 1) / num_seqs;
+    int64_t seg = ((avg + per_seq - 1) / per_seq + 15) / 16 * 16;
+    seg = std::max<int64_t>(seg, named ? 64 : 2048);
+    seg = std::min<int64_t>(seg, 1LL << 30);
+    const int64_t slots = num_seqs + (total_tokens + seg - 1) / seg;
+    return {static_cast<int32_t>(seg), static_cast<int32_t>(std::min<int64_t>(slots, 0x7fffffffLL))};
+}
+
+int32_t resolve_algo(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
+    int algo = cfg->algo;
+    if (algo == KDA_ALGO_AUTO) algo = cfg->io_dtype == KDA_DTYPE_BF16 ? KDA_ALGO_CHUNKED : KDA_ALGO_RECURRENT;
+    if (algo == KDA_ALGO_CHUNKED) {
+        // few (sequence, head) items over long sequences leave most CUs idle in one
+        // sequential pass: split the sequences (one 131072-token sequence x 96 heads)
+        const int64_t items = static_cast<int64_t>(num_seqs) * cfg->num_heads;
+        algo = scan_supported(cfg) && items < device_cu_count() && total_tokens >= 16384LL * num_seqs
+                   ? KDA_ALGO_CHUNKED_SCAN
+                   : KDA_ALGO_CHUNKED_THROUGHPUT;
+    }
+    return algo;
+}
+
+size_t workspace_bytes(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens, int32_t algo) {
+    if (algo != KDA_ALGO_CHUNKED_SCAN) return order_workspace_bytes(num_seqs);
+    const ScanPlan sp = scan_plan(cfg, num_seqs, total_tokens, cfg->algo == KDA_ALGO_CHUNKED_SCAN);
+    return scan_workspace_bytes(cfg->num_heads, num_seqs, sp.slots);
+}
+
 }  // namespace
 
 
@@ -131,14 +184,9 @@ void kda_config_init(kda_config *cfg, int32_t num_heads) {
     cfg->gate_rank = 128;
 }
 
-int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs) {
-    if (check_config(cfg) != KDA_OK || num_seqs <= 0) return -1;
-    int algo = cfg->algo;
-    if (algo == KDA_ALGO_AUTO) algo = cfg->io_dtype == KDA_DTYPE_BF16 ? KDA_ALGO_CHUNKED : KDA_ALGO_RECURRENT;
-    // the throughput variant is the faster one also where (sequence, head) items are
-    // fewer than CUs (one 131072-token sequence x 96 heads: 35 ms against 39 ms)
-    if (algo == KDA_ALGO_CHUNKED) algo = KDA_ALGO_CHUNKED_THROUGHPUT;
-    return algo;
+int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
+    if (check_config(cfg) != KDA_OK || num_seqs <= 0 || total_tokens < 0) return -1;
+    return resolve_algo(cfg, num_seqs, total_tokens);
 }
 
 kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens,
@@ -146,7 +194,7 @@ kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs, i
     kda_status st = check_config(cfg);
     if (st != KDA_OK) return st;
     if (!bytes || num_seqs <= 0 || total_tokens < 0) return KDA_ERR_INVALID_ARGUMENT;
-    *bytes = order_workspace_bytes(num_seqs);
+    *bytes = workspace_bytes(cfg, num_seqs, total_tokens, resolve_algo(cfg, num_seqs, total_tokens));
     return KDA_OK;
 }
 
@@ -166,10 +214,10 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
         !ok_ptr(a->state_out, false) || !ok_ptr(a->workspace, false) ||
         !ok_ptr(a->state_in_slots, false) || !ok_ptr(a->state_out_slots, false))
         return KDA_ERR_INVALID_ARGUMENT;
-    const size_t need = order_workspace_bytes(a->num_seqs);
+    const int algo = resolve_algo(cfg, a->num_seqs, a->total_tokens);
+    const size_t need = workspace_bytes(cfg, a->num_seqs, a->total_tokens, algo);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
-
-    const int algo = kda_prefill_resolved_algo(cfg, a->num_seqs);
+    if (algo == KDA_ALGO_CHUNKED_SCAN && !scan_supported(cfg)) return KDA_ERR_UNSUPPORTED;
     // the in-kernel low-rank gate runs on the matrix cores with bf16 factors (throughput
     // variant) or on the VALU (recurrent kernel); the pipelined variant does not have it
     if (lowrank_gate(cfg) &&
@@ -181,7 +229,10 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
         return KDA_ERR_UNSUPPORTED;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    int32_t *order = need > 0 ? static_cast<int32_t *>(a->workspace) : nullptr;
+    // the launches below are checked with hipGetLastError: drop an error another call of
+    // this thread left recorded in the (process-wide) runtime
+    (void)hipGetLastError();
+    int32_t *order = need > 0 && algo != KDA_ALGO_CHUNKED_SCAN ? static_cast<int32_t *>(a->workspace) : nullptr;
     if (order) {
         st = from_hip(launch_order(a->cu_seqlens, a->num_seqs, order, s));
         if (st != KDA_OK) return st;
@@ -207,7 +258,11 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
                 a->num_seqs, cfg->num_heads, static_cast<long long>(a->total_tokens), cfg->io_dtype,
                 cfg->out_dtype, algo, cfg->prologue, cfg->epilogue);
     hipError_t e;
-    if (algo == KDA_ALGO_CHUNKED_THROUGHPUT)
+    if (algo == KDA_ALGO_CHUNKED_SCAN) {
+        const ScanPlan sp = scan_plan(cfg, a->num_seqs, a->total_tokens, cfg->algo == KDA_ALGO_CHUNKED_SCAN);
+        if (trace_enabled()) fprintf(stderr, "[kda] scan: %d-token segments, %d slots\n", sp.seg_tokens, sp.slots);
+        e = launch_chunked_scan(p, cfg->out_dtype, a->num_seqs, sp.seg_tokens, sp.slots, a->workspace, s);
+    } else if (algo == KDA_ALGO_CHUNKED_THROUGHPUT)
         e = launch_chunked_throughput(p, cfg->io_dtype, cfg->out_dtype, s);
     else if (algo == KDA_ALGO_CHUNKED_LATENCY)
         e = launch_chunked_latency(p, cfg->io_dtype, cfg->out_dtype, s);
@@ -247,6 +302,7 @@ kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *a, void
     if (trace_enabled())
         fprintf(stderr, "[kda] decode B=%d H=%d io=%d out=%d\n", a->batch, cfg->num_heads,
                 cfg->io_dtype, cfg->out_dtype);
+    (void)hipGetLastError();  // as in kda_prefill
     return from_hip(launch_recurrent(p, cfg->io_dtype, cfg->out_dtype, static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -120,13 +120,63 @@ static_assert(2 * LDS_BYTES_LOWRANK <= 160 * 1024, "two workgroups per gfx950 CU
 constexpr float LOG2E = 1.4426950408889634f;
 
 
+// What a workgroup runs.  WHOLE: a whole sequence from its given state.  In the segmented
+// prefill, the first pass runs FIRST (segment 0, from the given state, entering state of
+// segment 1 out), M (a middle segment from S = I with v = 0: its transition matrix) and
+// B (the same segment from S = 0: its offset), and the second pass RERUNs segments 1 ..
+// from the state the scan gave them; only the last segment writes the final state and
+// conv cache.
+enum Role { WHOLE, FIRST, SEG_M, SEG_B, RERUN, SKIP };
+
+struct Place {
+    int n, h, len, role, slot;
+    int32_t ts;   // first token of the segment within the sequence
+    bool last;    // the sequence ends with this segment
+};
+
+__device__ __forceinline__ Place place_whole(const LayerParams &p, int item) {
+    Place w;
+    w.h = item % p.H;
+    const int idx = item / p.H;
+    w.n = p.order ? p.order[idx] : idx;
+    w.ts = 0;
+    w.len = p.cu_seqlens[w.n + 1] - p.cu_seqlens[w.n];
+    w.role = WHOLE;
+    w.slot = 0;
+    w.last = true;
+    return w;
+}
+
+// pass 1 items: [2][slots][H] (the second half runs B); pass 3 items: [slots][H]
+__device__ __forceinline__ Place place_segment(const LayerParams &p, int item) {
+    Place w;
+    const int per = p.seg_slots * p.H;
+    const int which = item / per;
+    const int rem = item - which * per;
+    w.slot = rem / p.H;
+    w.h = rem - w.slot * p.H;
+    const SegDesc d = p.seg[w.slot];
+    w.n = d.n;
+    w.ts = d.ts;
+    w.len = d.len;
+    w.last = d.p == d.np - 1;
+    if (d.n < 0)
+        w.role = SKIP;
+    else if (p.seg_pass == 1)
+        w.role = d.p == 0 ? (which ? SKIP : (w.last ? WHOLE : FIRST)) : (w.last ? SKIP : (which ? SEG_B : SEG_M));
+    else
+        w.role = d.p == 0 ? SKIP : RERUN;
+    return w;
+}
+
 // The second bound is waves per SIMD: two workgroups of 8 waves per CU need four
 // (at most 128 VGPRs).
 // GATE (KDA_GATE_*): log alpha read per channel, formed in the kernel from the low-rank
 // gate factors (bf16 io; K3's floored sigmoid or Kimi Linear's softplus), or read as one
 // value per (token, head).  WIDE: chunks whose decay leaves the factorised range take the
-// per-token path (decays without a floor).
-template <typename IO, typename OUT, int GATE, bool WIDE>
+// per-token path (decays without a floor).  SEG: a workgroup runs one segment of a
+// sequence in a pass of the segmented prefill (Role).
+template <typename IO, typename OUT, int GATE, bool WIDE, bool SEG>
 __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     constexpr bool SOFTPLUS = GATE == KDA_GATE_LOWRANK_SOFTPLUS;
     constexpr bool LOWRANK = GATE == KDA_GATE_LOWRANK || SOFTPLUS;
@@ -164,12 +214,14 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     int *const FLAG = reinterpret_cast<int *>(smem + OFF_FLAG);
 
     const int H = p.H;
-    const int item = blockIdx.x;
-    const int h = item % H;
-    const int idx = item / H;
-    const int n = p.order ? p.order[idx] : idx;
-    const int64_t t0 = p.cu_seqlens[n];
-    const int L = static_cast<int>(p.cu_seqlens[n + 1] - t0);
+    const Place pl = SEG ? place_segment(p, blockIdx.x) : place_whole(p, blockIdx.x);
+    if (pl.role == SKIP) return;  // the whole workgroup, before any barrier
+    const int h = pl.h;
+    const int n = pl.n;
+    const int64_t t0 = static_cast<int64_t>(p.cu_seqlens[n]) + pl.ts;  // first token of the run
+    const int L = pl.len;
+    const int role = pl.role;
+    const bool has_out = role == WHOLE || role == FIRST || role == RERUN;  // writes o
     const size_t HD = static_cast<size_t>(H) * D;
     const size_t hD = static_cast<size_t>(h) * D;
 
@@ -208,13 +260,21 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     // ---- state slice in accumulator layout: S[t][i] = S(16t + 4lh + i, col) ----------------
     const int row_in = p.slots_in ? p.slots_in[n] : n;     // state_in / conv_in row
     const int row_out = p.slots_out ? p.slots_out[n] : n;  // state_out / conv_out row
-    const size_t sbase = (static_cast<size_t>(row_in) * H + h) * D * D;
+    // entering state: the given one, the one the scan left in the previous slot's B, or
+    // (M) the identity, or (B) zero
+    const float *s_src = nullptr;
+    if ((role == WHOLE || role == FIRST) && p.state_in)
+        s_src = p.state_in + (static_cast<size_t>(row_in) * H + h) * D * D;
+    else if (SEG && role == RERUN)
+        s_src = p.seg_b + (static_cast<size_t>(pl.slot - 1) * H + h) * D * D;
     f32x4_t S[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[t][i] = p.state_in ? p.state_in[sbase + static_cast<size_t>(16 * t + 4 * lh + i) * D + col] : 0.0f;
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * t + 4 * lh + i;
+            S[t][i] = s_src ? s_src[static_cast<size_t>(r) * D + col] : (SEG && role == SEG_M && r == col ? 1.0f : 0.0f);
+        }
 
     const int nchunks = (L + C - 1) / C;
 
@@ -291,7 +351,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     auto load_gate = [&](int c) {
         const int x = opaque(tid);
         const int r0 = c * C, nrow = min(L, r0 + C) - r0;
-        if (p.epilogue)
+        if (p.epilogue && has_out)
             graw = IB::load(rows_view(g_base + static_cast<size_t>(r0) * rowb_io, nrow, rowb_io, D * sizeof(IO)),
                             static_cast<uint32_t>(x >> 5) * rowb_io + (x & 31) * 4 * sizeof(IO));
     };
@@ -307,7 +367,12 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         // history of the first chunk: the given conv cache (oldest first) or zeros
         const int s = tid / (CONV_HIST * 16), j = (tid / 16) % CONV_HIST, c0 = (tid & 15) * 8;
         float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (p.conv_in) IV::load(p.conv_in, ((static_cast<size_t>(row_in) * 3 + s) * CONV_HIST + j) * HD + hD + c0, x);
+        if (SEG && pl.ts > 0) {  // a later segment: the sequence's own preceding inputs
+            const void *srcs[3] = {p.q, p.k, p.v};
+            IV::load(srcs[s], static_cast<size_t>(t0 - CONV_HIST + j) * HD + hD + c0, x);
+        } else if (p.conv_in) {
+            IV::load(p.conv_in, ((static_cast<size_t>(row_in) * 3 + s) * CONV_HIST + j) * HD + hD + c0, x);
+        }
         store4f(RAW + (j * 3 + s) * D + c0, x);
         store4f(RAW + (j * 3 + s) * D + c0 + 4, x + 4);
     }
@@ -442,6 +507,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     for (int e = 0; e < 4; ++e) xq[e] = xk[e] = xv[e] = 0.0f;
                 }
             }
+        }
+        if (SEG && role == SEG_M) {  // the transition matrix: the recurrence with v = 0
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[e] = 0.0f;
         }
         if (HEADG) {
             if (tid == 0) {
@@ -772,7 +841,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         __syncthreads();
 
         // ---- 6. epilogue: sigma(g) * RMSNorm(o~) * w ------------------------------------------
-        {
+        if (!SEG || has_out) {
             float o[4];
             load4f((wide ? VB : OB) + et * FPK + ec0, o);
             if (p.epilogue) {
@@ -799,31 +868,40 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     }
 
     // ---- final state and conv cache ------------------------------------------------------
-    if (p.state_out) {
+    // a sequence's last run writes them; the segment passes leave M, or B / the state
+    // entering the next segment, in the workspace
+    const bool final_out = role == WHOLE || (SEG && role == RERUN && pl.last);
+    float *s_dst = nullptr;
+    if (final_out)
+        s_dst = p.state_out ? p.state_out + (static_cast<size_t>(row_out) * H + h) * D * D : nullptr;
+    else if (SEG && (role == FIRST || role == SEG_B))
+        s_dst = p.seg_b + (static_cast<size_t>(pl.slot) * H + h) * D * D;
+    else if (SEG && role == SEG_M)
+        s_dst = p.seg_m + (static_cast<size_t>(pl.slot) * H + h) * D * D;
+    if (s_dst) {
         const int x = opaque(tid);  // addresses built here, not kept live through the loop
-        float *const so = p.state_out + (static_cast<size_t>(row_out) * H + h) * D * D +
-                          static_cast<size_t>(4 * ((x & 63) >> 4)) * D + (x >> 6) * 16 + (x & 15);
+        float *const so = s_dst + static_cast<size_t>(4 * ((x & 63) >> 4)) * D + (x >> 6) * 16 + (x & 15);
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) so[(16 * t + i) * D] = S[t][i];
     }
-    if (p.prologue && p.conv_out) {
+    if (p.prologue && p.conv_out && final_out) {
         // the last three pre-conv inputs of each stream, oldest first; rows before the
         // sequence start come from conv_in (which conv_out may alias: read all, then write)
         const int task = tid;  // (stream, slot, channel group) = 3 * 3 * 16 = 144 tasks
         const bool active = task < 3 * CONV_HIST * 16;
         const int s = task / (CONV_HIST * 16), j = (task / 16) % CONV_HIST, cg = task & 15;
-        const int pj = L - CONV_HIST + j;  // source position
+        const int pj = L - CONV_HIST + j;  // source position, from the start of this run
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = 0.0f;
         const void *srcs[3] = {p.q, p.k, p.v};
         if (active) {
-            if (pj >= 0)
+            if (pl.ts + pj >= 0)
                 IV::load(srcs[s], static_cast<size_t>(t0 + pj) * HD + hD + cg * 8, x);
             else if (p.conv_in)
-                IV::load(p.conv_in, ((static_cast<size_t>(row_in) * 3 + s) * CONV_HIST + (CONV_HIST + pj)) * HD + hD + cg * 8, x);
+                IV::load(p.conv_in, ((static_cast<size_t>(row_in) * 3 + s) * CONV_HIST + (CONV_HIST + pl.ts + pj)) * HD + hD + cg * 8, x);
         }
         __syncthreads();
         if (active)
@@ -837,11 +915,11 @@ hipError_t launch(const LayerParams &p, hipStream_t s) {
     // log alpha with the floor of -5 never leaves the factorised range; without a floor the
     // chunks past it are found by the vote and take the per-token path
     if (p.gate == KDA_GATE_HEAD)
-        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_HEAD, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_HEAD, false, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     else if (p.gate == KDA_GATE_LOG_ALPHA_UNBOUNDED)
-        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_LOG_ALPHA, true>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_LOG_ALPHA, true, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     else
-        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_LOG_ALPHA, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_LOG_ALPHA, false, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     return hipGetLastError();
 }
 
@@ -851,15 +929,32 @@ hipError_t launch_lowrank(const LayerParams &p, hipStream_t s) {
     // K3's gate stays above its floor of -5 per token, so its chunks never leave the
     // factorised range; Kimi Linear's softplus gate has no floor
     if (p.gate == KDA_GATE_LOWRANK_SOFTPLUS)
-        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOWRANK_SOFTPLUS, true>), dim3(p.num_items),
+        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOWRANK_SOFTPLUS, true, false>), dim3(p.num_items),
                            dim3(THREADS), 0, s, p);
     else
-        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOWRANK, false>), dim3(p.num_items), dim3(THREADS),
+        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOWRANK, false, false>), dim3(p.num_items), dim3(THREADS),
                            0, s, p);
     return hipGetLastError();
 }
 
+template <typename OUT>
+hipError_t launch_segments(const LayerParams &p, int grid, hipStream_t s) {
+    if (p.gate == KDA_GATE_HEAD)
+        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_HEAD, false, true>), dim3(grid), dim3(THREADS), 0, s, p);
+    else if (p.gate == KDA_GATE_LOWRANK)
+        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOWRANK, false, true>), dim3(grid), dim3(THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOG_ALPHA, false, true>), dim3(grid), dim3(THREADS), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+// bf16 io and the floored gates only (checked by the caller)
+hipError_t launch_chunked_segments(const LayerParams &p, int out_dtype, int grid, hipStream_t s) {
+    if (grid <= 0) return hipSuccess;
+    return out_dtype == KDA_DTYPE_BF16 ? launch_segments<uint16_t>(p, grid, s) : launch_segments<float>(p, grid, s);
+}
 
 hipError_t launch_chunked_throughput(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s) {
     if (p.gate == KDA_GATE_LOWRANK || p.gate == KDA_GATE_LOWRANK_SOFTPLUS) {  // bf16 io only (checked by the caller)

@@ -12,6 +12,17 @@ namespace kda {
 constexpr int D = KDA_HEAD_DIM;  // d_k = d_v = 128
 constexpr int CONV_HIST = 3;     // kernel size 4 minus the current token
 
+// One segment of a sequence in the segmented prefill (KDA_ALGO_CHUNKED_SCAN).
+struct SegDesc {
+    int32_t n;      // sequence, or -1 for an unused slot
+    int32_t ts;     // first token of the segment, counted from the start of the sequence
+    int32_t len;    // tokens in the segment
+    int32_t p;      // index of the segment within its sequence
+    int32_t np;     // segments of the sequence
+    int32_t first;  // slot of the sequence's segment 0
+    int32_t pad0, pad1;
+};
+
 // Everything a kernel needs to know about one call.  Pointers are device
 // pointers; activations are token-major [tokens][H][128].
 struct LayerParams {
@@ -38,6 +49,12 @@ struct LayerParams {
     const void *gate_w;          // [H*128][r] io dtype
     const float *gate_bias;      // [H*128]
     const float *gate_a;         // [H]
+    // segmented prefill: the segment table, the pass (1: first segments, M and B of the
+    // middle ones; 3: the rerun of segments 1 ..), slots in the table, and the per (slot,
+    // head) fp32 [128][128] matrices M and B (B later holds the state entering slot + 1)
+    const SegDesc *seg;
+    int32_t seg_pass, seg_slots;
+    float *seg_m, *seg_b;
 };
 
 // ---------------------------------------------------------------- launchers
@@ -45,6 +62,12 @@ hipError_t launch_recurrent(const LayerParams &p, int io_dtype, int out_dtype, h
 hipError_t launch_chunked_throughput(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s);
 hipError_t launch_chunked_latency(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s);
 hipError_t launch_order(const int32_t *cu_seqlens, int32_t n, int32_t *order, hipStream_t s);
+// one pass of the segmented prefill over grid workgroups (bf16 io)
+hipError_t launch_chunked_segments(const LayerParams &p, int out_dtype, int grid, hipStream_t s);
+// the segmented prefill: table, first pass, scan of the segment transitions, rerun
+hipError_t launch_chunked_scan(LayerParams p, int out_dtype, int32_t num_seqs, int32_t seg_tokens,
+                               int32_t seg_slots, void *workspace, hipStream_t s);
+size_t scan_workspace_bytes(int32_t num_heads, int32_t num_seqs, int32_t seg_slots);
 size_t order_workspace_bytes(int32_t n);
 
 // ------------------------------------------------------------ device helpers

@@ -54,7 +54,7 @@ extern "C" {
 #endif
 
 #define KDA_HEAD_DIM 128
-#define KDA_ABI_VERSION 3u
+#define KDA_ABI_VERSION 4u
 
 /* Status codes. */
 typedef int32_t kda_status;
@@ -80,6 +80,19 @@ typedef int32_t kda_status;
 #define KDA_ALGO_CHUNKED 2              /* chunked, the variant the library prefers */
 #define KDA_ALGO_CHUNKED_THROUGHPUT 3   /* 8-wave workgroups, two per compute unit */
 #define KDA_ALGO_CHUNKED_LATENCY 4      /* one 8-wave producer/consumer workgroup per compute unit */
+/* CHUNKED_SCAN: the THROUGHPUT kernel over segments of each sequence, run in parallel.
+ * A chunk's effect on the state is affine, S -> M S + B (the composition that
+ * "Inside Kimi K3 ...", "KDA writes corrections into a recurrent matrix", unrolls
+ * token by token), so each segment but the first and last is run twice from S = I
+ * with v = 0 (its M) and from S = 0 (its B); the first segment runs from the given
+ * state.  A scan S_{p+1} = M_p S_p + B_p over the segments then gives every
+ * segment's entering state, and segments 1 .. P-1 run again from it to produce
+ * their outputs.  About 2.6x the arithmetic of one pass, for up to P-fold
+ * parallelism: AUTO takes it for bf16 inputs when the (sequence, head) items are
+ * fewer than the compute units and sequences average 16384 tokens or more, with
+ * about two segments per compute unit.  bf16 io and the LOG_ALPHA, LOWRANK and
+ * HEAD gates only; its M and B matrices live in the workspace. */
+#define KDA_ALGO_CHUNKED_SCAN 5
 
 /* Where the decay comes from ("Kimi K3 - KDA layer" step list: z_down = x W_down,
  * z = z_down W_up, alpha = exp(-5 sigmoid(e^A (z + b_alpha)))).  LOG_ALPHA: the
@@ -171,17 +184,21 @@ typedef struct {
     const float *gate_a;          /* [H] fp32: A_h (the multiplier is e^{A_h}) */
 } kda_prefill_args;
 
-/* Bytes of device workspace kda_prefill needs for N sequences (it holds the
- * longest-first order of the sequences).  Writes the size to *bytes. */
+/* Bytes of device workspace kda_prefill needs for N sequences of total_tokens
+ * tokens: the longest-first order of the sequences, or, when the algorithm resolves
+ * to CHUNKED_SCAN, the segment table and two fp32 128 x 128 matrices per (segment,
+ * head) (about 128 KiB x H x (N + total_tokens / segment length)).  Writes the
+ * size to *bytes. */
 kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
                                       int64_t total_tokens, size_t *bytes);
 
 kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *args, void *hip_stream);
 
-/* The KDA_ALGO_* that kda_prefill runs for this configuration and num_seqs
- * sequences (AUTO and CHUNKED resolved), or -1 when the configuration is
- * invalid or num_seqs <= 0.  Host only; enqueues nothing. */
-int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs);
+/* The KDA_ALGO_* that kda_prefill runs for this configuration, num_seqs sequences
+ * and total_tokens tokens on the current device (AUTO and CHUNKED resolved), or -1
+ * when the configuration is invalid, num_seqs <= 0 or total_tokens < 0.  Host only;
+ * enqueues nothing. */
+int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens);
 
 /* -------------------------------------------------------------- decode step
  * One token per request, the same layer core as prefill at T = 1 per

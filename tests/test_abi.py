@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_sizes():
-    assert kda.abi_version() == 3
+    assert kda.abi_version() == 4
     assert kda.state_bytes(96) == 96 * 128 * 128 * 4
     # the pages' per-request figure: 69 KDA layers x 12 heads per GPU at TP=8 x 128^2 x fp32
     assert abs(69 * kda.state_bytes(12) / 1e6 - 54.26) < 0.01
@@ -188,10 +188,34 @@ def test_resolved_algo():
         assert kda.resolved_algo(kda.config(4, algo=name), 2) == name
     assert kda.resolved_algo(kda.config(8), 1) == "chunked_throughput"
     assert kda.resolved_algo(kda.config(96, algo="chunked"), 4) == "chunked_throughput"
-    assert L.kda_prefill_resolved_algo(ctypes.byref(kda.config(4)), 0) == -1
+    assert L.kda_prefill_resolved_algo(ctypes.byref(kda.config(4)), 0, 0) == -1
+    assert L.kda_prefill_resolved_algo(ctypes.byref(kda.config(4)), 1, -1) == -1
     bad = kda.config(4)
     bad.algo = 9
-    assert L.kda_prefill_resolved_algo(ctypes.byref(bad), 1) == -1
+    assert L.kda_prefill_resolved_algo(ctypes.byref(bad), 1, 0) == -1
+
+
+def test_scan_selection_and_workspace():
+    """AUTO splits long sequences when (sequence, head) items are fewer than compute units
+    (256 when sized without a device); the workspace then holds two 64 KiB matrices per
+    (segment slot, head)."""
+    c = kda.config(96)
+    assert kda.resolved_algo(c, 1, 131072) == "chunked_scan"
+    assert kda.resolved_algo(c, 4, 16384) == "chunked_throughput"     # 384 items
+    assert kda.resolved_algo(c, 1, 8192) == "chunked_throughput"      # too short
+    assert kda.resolved_algo(kda.config(96, io_dtype="f32"), 1, 131072) == "recurrent"
+    assert kda.resolved_algo(kda.config(96, gate="lowrank_softplus"), 1, 131072) == "chunked_throughput"
+    assert kda.resolved_algo(kda.config(96, algo="chunked_throughput"), 1, 131072) == "chunked_throughput"
+    # one 131072-token sequence x 96 heads: 5 segments of 26224 tokens, 6 slots
+    assert kda.workspace_size(c, 1, 131072) == 256 + 256 + 2 * 6 * 96 * 128 * 128 * 4
+    # named: segments of at least 64 tokens (3 x 100 tokens, 2 heads: 3 + 5 slots)
+    s = kda.config(2, algo="chunked_scan")
+    assert kda.workspace_size(s, 3, 300) == 256 + 256 + 2 * 8 * 2 * 128 * 128 * 4
+    one = dict(num_seqs=1, workspace=None, workspace_bytes=0)
+    assert _prefill(kda.config(4, algo="chunked_scan", io_dtype="f32"), _args(**one)) == kda.ERR_WORKSPACE_TOO_SMALL
+    big = dict(num_seqs=1, workspace=FAKE, workspace_bytes=1 << 40)
+    assert _prefill(kda.config(4, algo="chunked_scan", io_dtype="f32"), _args(**big)) == kda.ERR_UNSUPPORTED
+    assert _prefill(kda.config(4, algo="chunked_scan", gate="log_alpha_unbounded"), _args(**big)) == kda.ERR_UNSUPPORTED
 
 
 def test_head_gate_arguments():

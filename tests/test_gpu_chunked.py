@@ -178,7 +178,7 @@ def test_full_size_prefill_sampled():
     inp = W.gen_prefill(spec)
     say("prefill_4x4096: gpu")
     g = gpu_prefill(inp, io="bf16", out="bf16", algo="auto")
-    assert kda.resolved_algo(kda.config(96), 4) == "chunked_throughput"
+    assert kda.resolved_algo(kda.config(96), 4, 16384) == "chunked_throughput"
     for seqs, heads in (([0], [0, 57]), ([3], [95])):
         sub = subset(inp, seqs, heads)
         r = oracle_prefill(sub)
@@ -191,16 +191,17 @@ def test_full_size_prefill_sampled():
 
 def test_long_context_sampled():
     """One 131072-token sequence, 96 heads, random fp32 S0 (the long-context launch):
-    sampled heads against the oracle, for the AUTO choice and the pipelined variant."""
+    sampled heads against the oracle, for the AUTO choice (the segmented prefill), the
+    throughput variant in one sequential pass, and the pipelined variant."""
     import gated_delta_rule_kda_amd as kda
     spec = W.workload("prefill_131072")
     say("prefill_131072: generating inputs")
     inp = W.gen_prefill(spec)
     say("prefill_131072: gpu")
-    assert kda.resolved_algo(kda.config(96), 1) == "chunked_throughput"
+    assert kda.resolved_algo(kda.config(96), 1, 131072) == "chunked_scan"
     heads = [3, 77]
     r = oracle_prefill(subset(inp, [0], heads))
-    for algo in ("auto", "chunked_latency"):
+    for algo in ("auto", "chunked_throughput", "chunked_latency"):
         g = gpu_prefill(inp, io="bf16", out="bf16", algo=algo)
         gs = gpu_rows(g, inp, [0], heads)
         say(f"  {algo}: heads {heads}")

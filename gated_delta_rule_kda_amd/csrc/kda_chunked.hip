@@ -222,6 +222,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     const int L = pl.len;
     const int role = pl.role;
     const bool has_out = role == WHOLE || role == FIRST || role == RERUN;  // writes o
+    // q enters only the outputs: the M and B runs of the segmented prefill skip its
+    // convolution, operands and products, and the M run (v = 0) the convolution of v
+    const bool qside = !SEG || has_out;
     const size_t HD = static_cast<size_t>(H) * D;
     const size_t hD = static_cast<size_t>(h) * D;
 
@@ -459,6 +462,11 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 #pragma unroll
             for (int s = 0; s < 3; ++s) {
                 float *a = outs[s];
+                if (SEG && ((s == 0 && !qside) || (s == 2 && role == SEG_M))) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] = 0.0f;
+                    continue;
+                }
                 if (p.prologue) {
                     float acc[4], w[4];
                     load4f(CW + (s * 4) * D + ec0, w);
@@ -591,9 +599,11 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             split4(kl, hi, lo);
             *reinterpret_cast<uint2 *>(KLh + at) = hi;
             *reinterpret_cast<uint2 *>(KLh + PL_CD + at) = lo;
-            split4(ql, hi, lo);
-            *reinterpret_cast<uint2 *>(QLh + at) = hi;
-            *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = lo;
+            if (qside) {
+                split4(ql, hi, lo);
+                *reinterpret_cast<uint2 *>(QLh + at) = hi;
+                *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = lo;
+            }
             split4(krd, hi, lo);
             *reinterpret_cast<uint2 *>(KRDh + at) = hi;
             *reinterpret_cast<uint2 *>(KRDh + PL_CD + at) = lo;
@@ -665,7 +675,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             if (ch + 1 < nchunks) load_current(ch + 1);
         } else {
             // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
-            if (wave < 2) {
+            if (wave == 0 || (wave == 1 && qside)) {
                 // the Gram blocks and T gate the next barrier for the whole workgroup: their
                 // waves take issue priority over the other waves of their SIMDs meanwhile
                 __builtin_amdgcn_s_setprio(2);
@@ -755,14 +765,16 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 const int ka = ln * OPK + 32 * s + 8 * lh;
                 const uint4 kh = *reinterpret_cast<const uint4 *>(KLh + ka);
                 const uint4 kl_ = *reinterpret_cast<const uint4 *>(KLh + PL_CD + ka);
-                const uint4 qh = *reinterpret_cast<const uint4 *>(QLh + ka);
-                const uint4 ql_ = *reinterpret_cast<const uint4 *>(QLh + PL_CD + ka);
                 const float v8[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
                                      S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
                 uint4 sh, sl;
                 split8(v8, sh, sl);
                 X = mma3(kh, kl_, sh, sl, X);
-                O1 = mma3(qh, ql_, sh, sl, O1);
+                if (qside) {
+                    const uint4 qh = *reinterpret_cast<const uint4 *>(QLh + ka);
+                    const uint4 ql_ = *reinterpret_cast<const uint4 *>(QLh + PL_CD + ka);
+                    O1 = mma3(qh, ql_, sh, sl, O1);
+                }
             }
             if (HEADG) {  // the row scales Gamma of Kbar = Diag(Gamma) K^ and Qbar = Diag(Gamma) Q^
                 const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
@@ -808,9 +820,11 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 const uint2 Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + ln * OPT + 4 * lh);
                 const f32x4_t Uf = mma16x2(Th, Tl, Xs.h, Xs.l, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 const Split4 Us(Uf);
-                const f32x4_t O = mma16x2(Ph, Pl, Us.h, Us.l, O1);  // Qbar S + P U
+                if (qside) {
+                    const f32x4_t O = mma16x2(Ph, Pl, Us.h, Us.l, O1);  // Qbar S + P U
 #pragma unroll
-                for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = O[i];
+                    for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = O[i];
+                }
                 if (late_decay) decay();
                 // Khat^T U with the products split as in mma16x2.  Rows of odd tiles hold their
                 // two token pairs swapped (the plane's bank swizzle), so those tiles take the

@@ -10,7 +10,12 @@ namespace kda {
 namespace chunk {
 
 constexpr int C = 16;          // tokens per chunk
-constexpr int OPK = D + 8;     // padded row (bf16 elements) of [16][128] operand planes
+// Padded row (bf16 elements) of the [16][128] operand planes: 288 bytes.  The MFMA
+// operand reads (lane: row l % 16, 16 bytes at column 8 (l / 16) of a 32-column step)
+// measured free of LDS bank conflicts with this stride on gfx950 and with no other
+// stride tried (272, 304 and 320 bytes, or XOR swizzles of the 16-byte groups); 272
+// bytes (the 16-byte minimum padding) cost a stall on most of these reads.
+constexpr int OPK = D + 16;
 constexpr int OPT = C + 4;     // padded row of [*][16] operand planes
 constexpr int FPK = D + 4;     // padded row (floats) of [16][128] fp32 tiles
 

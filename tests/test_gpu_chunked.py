@@ -207,3 +207,57 @@ def test_long_context_sampled():
         say(f"  {algo}: heads {heads}")
         _check(gs, r, "bf16")
         assert np.isfinite(g["o"]).all() and np.isfinite(g["state"]).all()
+
+
+def test_varlen_full_size_sampled():
+    """The packed variable-length launch as the benchmark times it: 64 sequences of
+    lognormal lengths (578k tokens), 96 heads, per-sequence S0, bf16 io and output, AUTO
+    algorithm.  Inputs are generated one sequence at a time straight into device buffers;
+    the longest, a median and the shortest sequence are regenerated on the host and
+    checked on one head each against the oracle."""
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    spec = W.workload("varlen_64")
+    lens = [int(x) for x in spec.lens]
+    N, H, T = len(lens), spec.heads, int(sum(lens))
+    dev, bf = torch.device("cuda:0"), torch.bfloat16
+    say(f"varlen_64: generating {T} tokens")
+    bufs = {k: torch.empty((T, H, W.D), dtype=bf, device=dev) for k in ("q", "k", "v", "g")}
+    la = torch.empty((T, H, W.D), dtype=torch.float32, device=dev)
+    beta = torch.empty((T, H), dtype=torch.float32, device=dev)
+    s0 = torch.empty((N, H, W.D, W.D), dtype=torch.float32, device=dev)
+    off, cw = 0, None
+
+    def seq(n):
+        return W.gen_prefill(W.PrefillSpec(lens=[lens[n]], heads=H, state_std=spec.state_std, seed=spec.seed,
+                                           first_seq=n))
+
+    for n, L in enumerate(lens):
+        x = seq(n)
+        for k in bufs:
+            bufs[k][off:off + L].copy_(torch.from_numpy(x[k]).to(bf))
+        la[off:off + L].copy_(torch.from_numpy(x["log_alpha"]))
+        beta[off:off + L].copy_(torch.from_numpy(x["beta"]))
+        s0[n].copy_(torch.from_numpy(x["state_in"][0]))
+        cw = x["conv_w"]
+        off += L
+        del x
+    cu_np = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu = torch.from_numpy(cu_np).to(dev)
+    say("varlen_64: gpu")
+    cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16")
+    o, s, _ = kda.prefill(bufs["q"], bufs["k"], bufs["v"], la, beta, cu, g=bufs["g"],
+                          conv_w=torch.from_numpy(cw).to(dev), state_in=s0, cfg=cfg, return_conv=False)
+    torch.cuda.synchronize()
+    del bufs, la, beta
+    order = np.argsort(lens)
+    for n, h in ((int(order[-1]), 7), (int(order[N // 2]), 45), (int(order[0]), 90)):
+        x = seq(n)
+        sub = subset(x, [0], [h])
+        r = oracle_prefill(sub)
+        g_o = o[int(cu_np[n]):int(cu_np[n + 1]), h].float().cpu().numpy().astype(np.float64)
+        g_s = s[n, h].cpu().numpy().astype(np.float64)
+        eo, es = err_bf16(g_o, r["o"][:, 0]), err(g_s, r["state"][0, 0])
+        say(f"  sequence {n} ({lens[n]} tokens) head {h}: o err {eo:.2e}  S err {es:.2e}")
+        assert eo <= BF16_TOL and es <= BF16_TOL
+    assert torch.isfinite(o).all()

@@ -345,11 +345,15 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     };
     auto load_w = [&]() {
         const int x = opaque(tid), xl = x & 63;
-        const uint16_t *w = static_cast<const uint16_t *>(p.gate_w) +
-                            (hD + (x >> 6) * 16 + (xl & 15)) * static_cast<size_t>(rank) + 8 * (xl >> 4);
+        const __amdgpu_buffer_rsrc_t wv =
+            rows_view(static_cast<const char *>(p.gate_w) + hD * rank * 2, D, rank * 2, rank * 2);
+        const uint32_t off = (static_cast<uint32_t>((x >> 6) * 16 + (xl & 15)) * rank + 8 * (xl >> 4)) * 2u;
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-            wb[st] = st < zsteps ? *reinterpret_cast<const uint4 *>(w + 32 * st) : make_uint4(0u, 0u, 0u, 0u);
+        for (int st = 0; st < 4; ++st) {
+            // a step past the rank reads past this lane's row: zeros
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(wv, st < zsteps ? off + 64u * st : 0x80000000u, 0, 0);
+            wb[st] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
     };
     auto load_gate = [&](int c) {
         const int x = opaque(tid);

@@ -11,8 +11,8 @@
 //   1. segment 0 of each sequence runs from the given state (outputs included) and
 //      leaves the state entering segment 1; every middle segment runs twice, for its
 //      M and its B (all in one launch);
-//   2. the scan below: S_{p+1} = M_p S_p + B_p for p = 1 .. P-2, in fp32, one
-//      workgroup per (sequence, head), written over B_p;
+//   2. the scan below: S_{p+1} = M_p S_p + B_p for p = 1 .. P-2, in fp32, eight
+//      workgroups per (sequence, head) over its value columns, written over B_p;
 //   3. segments 1 .. P-1 run again from their entering states, with outputs; the last
 //      one writes the final state and conv cache.
 // The same composition is what a split of one sequence over GPUs would exchange.
@@ -63,65 +63,57 @@ __global__ __launch_bounds__(256) void seg_table_kernel(const int32_t *cu, int32
     }
 }
 
-// S_{p+1} = M_p S_p + B_p over the middle segments of one (sequence, head).  S_p is
-// staged in LDS (fp32, 64 KiB); M_p is read from memory (it stays in the caches: each
-// element is read by the 16 threads of a row group).  Thread x computes rows
-// 4(x/16) .. +3 and columns 8(x%16) .. +7 of the product in fp32.  B_p is overwritten in
-// place with S_{p+1}, which the rerun of segment p+1 reads.
+// S_{p+1} = M_p S_p + B_p over the middle segments of one (sequence, head), for 16 of
+// its 128 value columns (the columns evolve independently: M acts on the key side), so
+// that eight workgroups share each (sequence, head).  The 128 x 16 slice of S_p is staged
+// in LDS; thread x computes row x / 4, columns 4 (x % 4) .. +3 of the slice in fp32, with
+// M_p's row read from memory four elements at a time (it stays in the caches).  B_p is
+// overwritten in place with S_{p+1}, which the rerun of segment p+1 reads.
+constexpr int COMBINE_COLS = 16;
+constexpr int COMBINE_GROUPS = D / COMBINE_COLS;
 __global__ __launch_bounds__(SCAN_THREADS) void seg_combine_kernel(const int32_t *firsts, int32_t H,
                                                                    const float *mm, float *bb) {
-    __shared__ __attribute__((aligned(16))) float SS[D * D];  // the current entering state
-    const int n = blockIdx.x / H, h = blockIdx.x % H;
+    __shared__ __attribute__((aligned(16))) float SS[D * COMBINE_COLS];  // S_p[:, cols]
+    const int cg = blockIdx.x % COMBINE_GROUPS;
+    const int nh = blockIdx.x / COMBINE_GROUPS;
+    const int n = nh / H, h = nh % H;
     const int32_t first = firsts[n], np = firsts[n + 1] - firsts[n];
     if (np < 3) return;  // nothing between the first and the last segment
     const int tid = threadIdx.x;
-    const int i0 = 4 * (tid >> 4), j0 = 8 * (tid & 15);
+    const int r = tid >> 2, c0 = 4 * (tid & 3);   // output row, first of 4 columns of the slice
+    const int col = cg * COMBINE_COLS;
     const size_t mat = static_cast<size_t>(D) * D;
     // S_1, left by segment 0's run in its B slot
-    const float *src = bb + (static_cast<size_t>(first) * H + h) * mat;
-    for (int e = tid; e < D * D / 4; e += SCAN_THREADS)
-        reinterpret_cast<float4 *>(SS)[e] = reinterpret_cast<const float4 *>(src)[e];
+    {
+        const float *src = bb + (static_cast<size_t>(first) * H + h) * mat;
+        *reinterpret_cast<float4 *>(SS + r * COMBINE_COLS + c0) =
+            *reinterpret_cast<const float4 *>(src + static_cast<size_t>(r) * D + col + c0);
+    }
     __syncthreads();
     for (int32_t q = 1; q + 1 < np; ++q) {
         const size_t off = (static_cast<size_t>(first + q) * H + h) * mat;
-        const float *m = mm + off + static_cast<size_t>(i0) * D;
-        float *b = bb + off;
-        float acc[4][8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) acc[r][c] = 0.0f;
+        const float *m = mm + off + static_cast<size_t>(r) * D;
+        float *const b = bb + off + static_cast<size_t>(r) * D + col + c0;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
         for (int k0 = 0; k0 < D; k0 += 4) {
-            float4 mr[4];  // M[i0 + r][k0 .. k0 + 3]
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mr[r] = *reinterpret_cast<const float4 *>(m + r * D + k0);
+            const float4 m4 = *reinterpret_cast<const float4 *>(m + k0);
+            const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const float4 s0 = *reinterpret_cast<const float4 *>(SS + (k0 + kk) * D + j0);
-                const float4 s1 = *reinterpret_cast<const float4 *>(SS + (k0 + kk) * D + j0 + 4);
-                const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float mv = kk == 0 ? mr[r].x : kk == 1 ? mr[r].y : kk == 2 ? mr[r].z : mr[r].w;
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(mv, sv[c], acc[r][c]);
-                }
+                const float4 s4 = *reinterpret_cast<const float4 *>(SS + (k0 + kk) * COMBINE_COLS + c0);
+                acc[0] = fmaf(mv[kk], s4.x, acc[0]);
+                acc[1] = fmaf(mv[kk], s4.y, acc[1]);
+                acc[2] = fmaf(mv[kk], s4.z, acc[2]);
+                acc[3] = fmaf(mv[kk], s4.w, acc[3]);
             }
         }
+        const float4 b4 = *reinterpret_cast<const float4 *>(b);
+        const float4 nx = make_float4(acc[0] + b4.x, acc[1] + b4.y, acc[2] + b4.z, acc[3] + b4.w);
+        *reinterpret_cast<float4 *>(b) = nx;
         __syncthreads();  // every thread is done with SS
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float4 *const bo = reinterpret_cast<float4 *>(b + static_cast<size_t>(i0 + r) * D + j0);
-            float4 *const so = reinterpret_cast<float4 *>(SS + (i0 + r) * D + j0);
-            const float4 b0 = bo[0], b1 = bo[1];
-            const float4 n0 = make_float4(acc[r][0] + b0.x, acc[r][1] + b0.y, acc[r][2] + b0.z, acc[r][3] + b0.w);
-            const float4 n1 = make_float4(acc[r][4] + b1.x, acc[r][5] + b1.y, acc[r][6] + b1.z, acc[r][7] + b1.w);
-            bo[0] = n0;
-            bo[1] = n1;
-            so[0] = n0;
-            so[1] = n1;
-        }
-        __syncthreads();  // SS holds S_{q+1} before the next product reads it
+        *reinterpret_cast<float4 *>(SS + r * COMBINE_COLS + c0) = nx;
+        __syncthreads();  // SS holds the slice of S_{q+1}
     }
 }
 
@@ -165,8 +157,8 @@ hipError_t launch_chunked_scan(LayerParams p, int out_dtype, int32_t num_seqs, i
     p.seg_pass = 1;
     e = stage(launch_chunked_segments(p, out_dtype, 2 * seg_slots * p.H, s), "first pass");
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(seg_combine_kernel, dim3(num_seqs * p.H), dim3(SCAN_THREADS), 0, s, firsts, p.H, p.seg_m,
-                       p.seg_b);
+    hipLaunchKernelGGL(seg_combine_kernel, dim3(num_seqs * p.H * COMBINE_GROUPS), dim3(SCAN_THREADS), 0, s, firsts,
+                       p.H, p.seg_m, p.seg_b);
     e = stage(hipGetLastError(), "combine");
     if (e != hipSuccess) return e;
     p.seg_pass = 3;

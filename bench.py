@@ -106,6 +106,34 @@ def load_traffic(path: str) -> dict:
     return out
 
 
+def oracle_single_thread(W, oracle, decode_sample: int = 16) -> dict:
+    """The oracle on one thread: the whole 256-token x 2-head core case (fp32 io, no
+    projections around the recurrence), and the first `decode_sample` requests of the
+    256-request decode step (all 96 heads, full layer), scaled to requests per second."""
+    out = {}
+    spec = W.workload("core_fp32")
+    x = W.gen_prefill(spec)
+    t0 = time.perf_counter()
+    oracle.prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], x["cu_seqlens"],
+                   prologue=False, epilogue=False, threads=1)
+    ct = time.perf_counter() - t0
+    T = int(x["cu_seqlens"][-1])
+    out["core_fp32"] = {"value": T / ct, "unit": "tokens/s", "ms": ct * 1e3, "cores": 1,
+                        "sample": f"whole workload: {T} tokens x {spec.heads} heads"}
+    dspec = W.workload("decode_256")
+    y = W.gen_decode(dspec)
+    b = min(decode_sample, dspec.batch)
+    t0 = time.perf_counter()
+    oracle.decode_step(y["q"][:b], y["k"][:b], y["v"][:b], y["log_alpha"][:b], y["beta"][:b],
+                       y["state"][:b], g=y["g"][:b], conv_w=y["conv_w"],
+                       conv_state=y["conv_state"][:b], threads=1)
+    ct = time.perf_counter() - t0
+    out["decode_256"] = {"value": b / ct, "unit": "requests/s", "ms_per_step": dspec.batch / b * ct * 1e3,
+                         "cores": 1, "sample": f"{b} of {dspec.batch} requests x {dspec.heads} heads, "
+                                               f"scaled to the whole step"}
+    return out
+
+
 def run_extra_workloads(kda, W, dev, stream, log, algo="auto") -> dict:
     """Time the long-context (1 x 131072) and packed variable-length (64 sequences)
     prefills, and the long context at 12 heads (one GPU's share of 96 heads split eight
@@ -465,7 +493,7 @@ def main() -> int:
     algo_name = kda.resolved_algo(cfg, N)
 
     # ---------------------------------------------------------------- CPU oracle
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         import oracle
         threads = len(os.sched_getaffinity(0))
@@ -479,6 +507,8 @@ def main() -> int:
                "sample": f"sequence 0 of the prefill workload: {L0} tokens x {H} heads, full layer, "
                          f"fp64, {ct:.1f}s wall on {threads} threads ({cpu_info()})"}
         log(f"oracle: {L0} tokens x {H} heads in {ct:.1f}s on {threads} threads")
+        cpu1 = oracle_single_thread(W, oracle)
+        log(f"oracle, one thread: {json.dumps(cpu1)}")
 
     traffic = load_traffic(args.traffic)
     extra = None
@@ -523,6 +553,8 @@ def main() -> int:
                             "traffic": traffic.get("decode")},
         "cpu_baseline": cpu,
     }
+    if cpu1:
+        res["cpu_baseline_1thread"] = cpu1
     if copy_cal:
         res["copy_calibration"] = copy_cal
     if extra:

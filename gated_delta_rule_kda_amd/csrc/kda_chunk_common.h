@@ -47,6 +47,64 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
 }
 
+// The same splits with the residuals x - hi taken from the bf16 dot product
+// x + (hi_a, hi_b) . (-1, 0) (and (0, -1)), which is exact (x - hi has at most 16
+// significant bits) and one instruction per element instead of three.  The compiler does
+// not emit the three-operand form of that instruction, so these are written out; inside,
+// each residual is read at least three instructions after the dot product that writes it,
+// and a final wait of three covers a matrix-core read of the results.  The inputs must be
+// vector-ALU results, not fresh matrix-core accumulators: the compiler does not see the
+// instructions inside and so inserts no wait for that dependence.
+__device__ __forceinline__ void split8_dot(const float *x, uint4 &hi, uint4 &lo) {
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    float r0, r1, r2, r3, r4, r5, r6, r7;
+    const uint32_t na = 0x0000bf80u, nb = 0xbf800000u;  // bf16 pairs (-1, 0) and (0, -1)
+    asm volatile(
+        "v_cvt_pk_bf16_f32 %0, %16, %17\n\t"
+        "v_cvt_pk_bf16_f32 %1, %18, %19\n\t"
+        "v_cvt_pk_bf16_f32 %2, %20, %21\n\t"
+        "v_cvt_pk_bf16_f32 %3, %22, %23\n\t"
+        "v_dot2_f32_bf16 %8, %0, %24, %16\n\t"
+        "v_dot2_f32_bf16 %9, %0, %25, %17\n\t"
+        "v_dot2_f32_bf16 %10, %1, %24, %18\n\t"
+        "v_dot2_f32_bf16 %11, %1, %25, %19\n\t"
+        "v_dot2_f32_bf16 %12, %2, %24, %20\n\t"
+        "v_dot2_f32_bf16 %13, %2, %25, %21\n\t"
+        "v_dot2_f32_bf16 %14, %3, %24, %22\n\t"
+        "v_dot2_f32_bf16 %15, %3, %25, %23\n\t"
+        "v_cvt_pk_bf16_f32 %4, %8, %9\n\t"
+        "v_cvt_pk_bf16_f32 %5, %10, %11\n\t"
+        "v_cvt_pk_bf16_f32 %6, %12, %13\n\t"
+        "v_cvt_pk_bf16_f32 %7, %14, %15\n\t"
+        "s_nop 2"
+        : "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3), "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3),
+          "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "s"(na), "s"(nb));
+    hi = make_uint4(h0, h1, h2, h3);
+    lo = make_uint4(l0, l1, l2, l3);
+}
+
+__device__ __forceinline__ void split4_dot(const float *x, uint2 &hi, uint2 &lo) {
+    uint32_t h0, h1, l0, l1;
+    float r0, r1, r2, r3;
+    const uint32_t na = 0x0000bf80u, nb = 0xbf800000u;
+    asm volatile(
+        "v_cvt_pk_bf16_f32 %0, %8, %9\n\t"
+        "v_cvt_pk_bf16_f32 %1, %10, %11\n\t"
+        "v_dot2_f32_bf16 %4, %0, %12, %8\n\t"
+        "v_dot2_f32_bf16 %5, %0, %13, %9\n\t"
+        "v_dot2_f32_bf16 %6, %1, %12, %10\n\t"
+        "v_dot2_f32_bf16 %7, %1, %13, %11\n\t"
+        "s_nop 1\n\t"
+        "v_cvt_pk_bf16_f32 %2, %4, %5\n\t"
+        "v_cvt_pk_bf16_f32 %3, %6, %7\n\t"
+        "s_nop 2"
+        : "=&v"(h0), "=&v"(h1), "=&v"(l0), "=&v"(l1), "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "s"(na), "s"(nb));
+    hi = make_uint2(h0, h1);
+    lo = make_uint2(l0, l1);
+}
+
 __device__ __forceinline__ void split8(const float *x, uint4 &hi, uint4 &lo) {
     split2(x[0], x[1], hi.x, lo.x);
     split2(x[2], x[3], hi.y, lo.y);
@@ -81,6 +139,7 @@ __device__ __forceinline__ f32x4_t mma16_3(uint2 ahi, uint2 alo, uint2 bhi, uint
 // A 16x16 fp32 matrix fragment (4 values per lane) split into bf16 hi/lo.
 struct Split4 {
     uint2 h, l;
+    Split4() = default;
     __device__ __forceinline__ explicit Split4(const float *x) { split4(x, h, l); }
     __device__ __forceinline__ explicit Split4(const f32x4_t &x) {
         const float v[4] = {x[0], x[1], x[2], x[3]};

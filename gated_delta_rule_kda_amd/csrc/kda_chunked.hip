@@ -568,10 +568,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             // k^ and q^ unscaled; the k^ split also fills the transposed Khat^T plane
             const int at = et * OPK + cperm(ec0);
             uint2 hi, lo;
-            split4(xq, hi, lo);
+            split4_dot(xq, hi, lo);
             *reinterpret_cast<uint2 *>(QLh + at) = hi;
             *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = lo;
-            split4(xk, hi, lo);
+            split4_dot(xk, hi, lo);
             *reinterpret_cast<uint2 *>(KLh + at) = hi;
             *reinterpret_cast<uint2 *>(KLh + PL_CD + at) = lo;
             const uint32_t hw[4] = {hi.x, hi.x >> 16, hi.y, hi.y >> 16};
@@ -600,19 +600,19 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             // channels ec0 .. ec0+3 keep their order at channel-permuted position cperm(ec0)
             const int at = et * OPK + cperm(ec0);
             uint2 hi, lo;
-            split4(kl, hi, lo);
+            split4_dot(kl, hi, lo);
             *reinterpret_cast<uint2 *>(KLh + at) = hi;
             *reinterpret_cast<uint2 *>(KLh + PL_CD + at) = lo;
             if (qside) {
-                split4(ql, hi, lo);
+                split4_dot(ql, hi, lo);
                 *reinterpret_cast<uint2 *>(QLh + at) = hi;
                 *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = lo;
             }
-            split4(krd, hi, lo);
+            split4_dot(krd, hi, lo);
             *reinterpret_cast<uint2 *>(KRDh + at) = hi;
             *reinterpret_cast<uint2 *>(KRDh + PL_CD + at) = lo;
             // Khat^T[c][t] = k^_t[c] e^{G_C[c] - G_t[c]}
-            split4(kht, hi, lo);
+            split4_dot(kht, hi, lo);
             const uint32_t hw[4] = {hi.x, hi.x >> 16, hi.y, hi.y >> 16};
             const uint32_t lw[4] = {lo.x, lo.x >> 16, lo.y, lo.y >> 16};
 #pragma unroll
@@ -722,11 +722,19 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     __builtin_amdgcn_wave_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
                     const int x = opaque(lane), j = x >> 2, r = x & 3;
+                    // step k's A column is read TD steps ahead, so that the dependent chain of
+                    // the substitution does not wait on LDS every other step
+                    constexpr int TD = 6;
+                    float4 af[C];
+#pragma unroll
+                    for (int k = 0; k < TD; ++k) af[k] = *reinterpret_cast<const float4 *>(AF + k * AFK + 4 * r);
                     float xv[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) xv[q] = (4 * q + r == j) ? 1.0f : 0.0f;
 #pragma unroll
                     for (int k = 0; k < C; ++k) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (k + TD < C) af[k + TD] = *reinterpret_cast<const float4 *>(AF + (k + TD) * AFK + 4 * r);
                         float xk;
                         switch (k & 3) {  // x_k, from lane 4j + k % 4 of the quad
                             case 0: xk = dpp<0x00>(xv[k >> 2]); break;
@@ -734,7 +742,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                             case 2: xk = dpp<0xAA>(xv[k >> 2]); break;
                             default: xk = dpp<0xFF>(xv[k >> 2]); break;
                         }
-                        const float4 a = *reinterpret_cast<const float4 *>(AF + k * AFK + 4 * r);
+                        const float4 a = af[k];
                         xv[0] = fmaf(-a.x, xk, xv[0]);
                         xv[1] = fmaf(-a.y, xk, xv[1]);
                         xv[2] = fmaf(-a.z, xk, xv[2]);
@@ -772,7 +780,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 const float v8[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
                                      S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
                 uint4 sh, sl;
-                split8(v8, sh, sl);
+                split8_dot(v8, sh, sl);
                 X = mma3(kh, kl_, sh, sl, X);
                 if (qside) {
                     const uint4 qh = *reinterpret_cast<const uint4 *>(QLh + ka);
@@ -792,7 +800,11 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) X[i] = VB[(4 * lh + i) * FPK + col] - X[i];
-            const Split4 Xs(X);
+            Split4 Xs;
+            {
+                const float x4[4] = {X[0], X[1], X[2], X[3]};
+                split4_dot(x4, Xs.h, Xs.l);
+            }
             // S has been read: decay it now, S <- Diag(Gamma_C) S, in the time the Gram / T
             // waves need before the barrier (they decay theirs after it)
             const bool late_decay = wave == 0;

@@ -355,15 +355,25 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             wb[st] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     };
+    // Issued on every path, past the last chunk too (an empty view reads zeros without a
+    // memory access), so that the wait for a chunk's rows always counts the same younger
+    // memory operations and never has to wait for the output stores as well.
     auto load_gate = [&](int c) {
         const int x = opaque(tid);
-        const int r0 = c * C, nrow = min(L, r0 + C) - r0;
-        if (p.epilogue && has_out)
-            graw = IB::load(rows_view(g_base + static_cast<size_t>(r0) * rowb_io, nrow, rowb_io, D * sizeof(IO)),
-                            static_cast<uint32_t>(x >> 5) * rowb_io + (x & 31) * 4 * sizeof(IO));
+        const int r0 = c * C;
+        const bool use = p.epilogue && has_out;
+        const int nrow = use ? min(L, r0 + C) - r0 : 0;
+        const char *const gb = use ? g_base + static_cast<size_t>(r0) * rowb_io : static_cast<const char *>(p.q);
+        graw = IB::load(rows_view(gb, nrow, rowb_io, D * sizeof(IO)),
+                        static_cast<uint32_t>(x >> 5) * rowb_io + (x & 31) * 4 * sizeof(IO));
     };
     if (nchunks > 0) {
         load_current(0);
+        // an empty store (its view has no bytes, so it is dropped without a memory access)
+        // where the loop has the previous chunk's output store: the same memory operations
+        // then follow a chunk's rows on both ways into the loop, and the wait for the rows
+        // at the top of the loop need not cover the output store
+        __builtin_amdgcn_raw_buffer_store_b32(0u, rows_view(o_base, 0, 0, 0), 0u, 0, 0);
         load_gate(0);
         if (LOWRANK) {
             load_z(0);
@@ -414,6 +424,8 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         if ((tid & 31) == 0) BETA[et] = bet;
         if (WIDE && tid == 0) *FLAG = 0;
         if (LOWRANK) load_w();  // this lane's W_up operand, used right after the barrier
+        // the next chunk's rows: a whole chunk of work hides their latency
+        if (ch + 1 < nchunks) load_current(ch + 1);
         __syncthreads();
 
         // ---- 2. conv4 + SiLU (+ L2 for q, k) from the staged rows; cumulative log-decay -------
@@ -676,7 +688,6 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 const float o = row_group_sum((o4[0] + o4[1]) + (o4[2] + o4[3]));
                 if (lrow == 0) VB[u * FPK + lcol] = o;
             }
-            if (ch + 1 < nchunks) load_current(ch + 1);
         } else {
             // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
             if (wave == 0 || (wave == 1 && qside)) {
@@ -828,7 +839,6 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             __syncthreads();
 
             // ---- 5. U = T X, O = scale (Qbar S + P U), S <- Diag(Gamma_C) S + Khat^T U -------------
-            if (ch + 1 < nchunks) load_current(ch + 1);
             {
                 const uint2 Th = *reinterpret_cast<const uint2 *>(TMh + ln * OPT + 4 * lh);
                 const uint2 Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh);
@@ -890,10 +900,8 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                                             static_cast<uint32_t>(HD * sizeof(OUT)), D * sizeof(OUT)),
                                   static_cast<uint32_t>(et) * static_cast<uint32_t>(HD * sizeof(OUT)) + ec0 * sizeof(OUT), o);
         }
-        if (ch + 1 < nchunks) {
-            load_gate(ch + 1);
-            if (LOWRANK) load_z(ch + 1);
-        }
+        load_gate(ch + 1);
+        if (LOWRANK) load_z(ch + 1);
         // the next chunk's first two barriers order these LDS reads before any rewrite
     }
 

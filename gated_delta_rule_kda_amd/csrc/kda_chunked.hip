@@ -278,6 +278,11 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             const int r = 16 * t + 4 * lh + i;
             S[t][i] = s_src ? s_src[static_cast<size_t>(r) * D + col] : (SEG && role == SEG_M && r == col ? 1.0f : 0.0f);
         }
+    // Settle the state loads here, once: the state's first readers in the loop are written
+    // out as assembly, and without this the compiler waits for every outstanding memory
+    // operation before them in each chunk (the next chunk's rows included).
+#pragma unroll
+    for (int t = 0; t < 8; ++t) asm volatile("" : "+v"(S[t]));
 
     const int nchunks = (L + C - 1) / C;
 
@@ -367,19 +372,6 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         graw = IB::load(rows_view(gb, nrow, rowb_io, D * sizeof(IO)),
                         static_cast<uint32_t>(x >> 5) * rowb_io + (x & 31) * 4 * sizeof(IO));
     };
-    if (nchunks > 0) {
-        load_current(0);
-        // an empty store (its view has no bytes, so it is dropped without a memory access)
-        // where the loop has the previous chunk's output store: the same memory operations
-        // then follow a chunk's rows on both ways into the loop, and the wait for the rows
-        // at the top of the loop need not cover the output store
-        __builtin_amdgcn_raw_buffer_store_b32(0u, rows_view(o_base, 0, 0, 0), 0u, 0, 0);
-        load_gate(0);
-        if (LOWRANK) {
-            load_z(0);
-            load_w();
-        }
-    }
     if (p.prologue && tid < 3 * CONV_HIST * 16) {
         // history of the first chunk: the given conv cache (oldest first) or zeros
         const int s = tid / (CONV_HIST * 16), j = (tid / 16) % CONV_HIST, c0 = (tid & 15) * 8;
@@ -394,6 +386,19 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         store4f(RAW + (j * 3 + s) * D + c0 + 4, x + 4);
     }
 
+    if (nchunks > 0) {
+        load_current(0);
+        // an empty store (its view has no bytes, so it is dropped without a memory access)
+        // where the loop has the previous chunk's output store: the same memory operations
+        // then follow a chunk's rows on both ways into the loop, and the wait for the rows
+        // at the top of the loop need not cover the output store
+        __builtin_amdgcn_raw_buffer_store_b32(0u, rows_view(o_base, 0, 0, 0), 0u, 0, 0);
+        load_gate(0);
+        if (LOWRANK) {
+            load_z(0);
+            load_w();
+        }
+    }
     // this thread's staged row (position et) and the same row three positions earlier
     float *const raw_t = RAW + ((CONV_HIST + et) * 3) * D + ec0;
 
@@ -424,8 +429,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         if ((tid & 31) == 0) BETA[et] = bet;
         if (WIDE && tid == 0) *FLAG = 0;
         if (LOWRANK) load_w();  // this lane's W_up operand, used right after the barrier
-        // the next chunk's rows: a whole chunk of work hides their latency
-        if (ch + 1 < nchunks) load_current(ch + 1);
+        // the next chunk's rows: a whole chunk of work hides their latency (past the last
+        // chunk the views are empty: zeros, no memory access, and the same count of memory
+        // operations on every path, so that later waits stay exact)
+        load_current(ch + 1);
         __syncthreads();
 
         // ---- 2. conv4 + SiLU (+ L2 for q, k) from the staged rows; cumulative log-decay -------
@@ -899,6 +906,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             OutStore4<OUT>::store(rows_view(o_base + static_cast<size_t>(r0) * HD * sizeof(OUT), rend - r0,
                                             static_cast<uint32_t>(HD * sizeof(OUT)), D * sizeof(OUT)),
                                   static_cast<uint32_t>(et) * static_cast<uint32_t>(HD * sizeof(OUT)) + ec0 * sizeof(OUT), o);
+        } else {
+            // runs without outputs still issue one (empty, dropped) store, so that every path
+            // leaves the same memory operations behind the next chunk's rows
+            __builtin_amdgcn_raw_buffer_store_b32(0u, rows_view(o_base, 0, 0, 0), 0u, 0, 0);
         }
         load_gate(ch + 1);
         if (LOWRANK) load_z(ch + 1);

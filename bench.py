@@ -374,7 +374,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--algo", default="auto",
                     choices=["auto", "recurrent", "chunked", "chunked_throughput", "chunked_latency"])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -49,60 +49,68 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
 
 // The same splits with the residuals x - hi taken from the bf16 dot product
 // x + (hi_a, hi_b) . (-1, 0) (and (0, -1)), which is exact (x - hi has at most 16
-// significant bits) and one instruction per element instead of three.  The compiler does
-// not emit the three-operand form of that instruction, so these are written out; inside,
-// each residual is read at least three instructions after the dot product that writes it,
-// and a final wait of three covers a matrix-core read of the results.  The inputs must be
-// vector-ALU results, not fresh matrix-core accumulators: the compiler does not see the
-// instructions inside and so inserts no wait for that dependence.
-__device__ __forceinline__ void split8_dot(const float *x, uint4 &hi, uint4 &lo) {
-    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-    float r0, r1, r2, r3, r4, r5, r6, r7;
+// significant bits) and one instruction per element instead of three.  The compiler emits
+// only the accumulator-tied form of that instruction, so the dot products alone are written
+// out, in groups of four pairs; the conversions before and after them stay the compiler's,
+// which therefore keeps the waits it owes the producers of x (a matrix-core result, say) and
+// the consumers of the hi and lo parts.  The one wait it cannot see, a dot product's result
+// read by another vector instruction, is the trailing s_nop: three wait states after the
+// last dot product, and more after the earlier ones.
+__device__ __forceinline__ void dot_residuals4(const uint32_t *h, const float *x, float *r) {
     const uint32_t na = 0x0000bf80u, nb = 0xbf800000u;  // bf16 pairs (-1, 0) and (0, -1)
     asm volatile(
-        "v_cvt_pk_bf16_f32 %0, %16, %17\n\t"
-        "v_cvt_pk_bf16_f32 %1, %18, %19\n\t"
-        "v_cvt_pk_bf16_f32 %2, %20, %21\n\t"
-        "v_cvt_pk_bf16_f32 %3, %22, %23\n\t"
-        "v_dot2_f32_bf16 %8, %0, %24, %16\n\t"
-        "v_dot2_f32_bf16 %9, %0, %25, %17\n\t"
-        "v_dot2_f32_bf16 %10, %1, %24, %18\n\t"
-        "v_dot2_f32_bf16 %11, %1, %25, %19\n\t"
-        "v_dot2_f32_bf16 %12, %2, %24, %20\n\t"
-        "v_dot2_f32_bf16 %13, %2, %25, %21\n\t"
-        "v_dot2_f32_bf16 %14, %3, %24, %22\n\t"
-        "v_dot2_f32_bf16 %15, %3, %25, %23\n\t"
-        "v_cvt_pk_bf16_f32 %4, %8, %9\n\t"
-        "v_cvt_pk_bf16_f32 %5, %10, %11\n\t"
-        "v_cvt_pk_bf16_f32 %6, %12, %13\n\t"
-        "v_cvt_pk_bf16_f32 %7, %14, %15\n\t"
+        "v_dot2_f32_bf16 %0, %8, %12, %14\n\t"
+        "v_dot2_f32_bf16 %1, %8, %13, %15\n\t"
+        "v_dot2_f32_bf16 %2, %9, %12, %16\n\t"
+        "v_dot2_f32_bf16 %3, %9, %13, %17\n\t"
+        "v_dot2_f32_bf16 %4, %10, %12, %18\n\t"
+        "v_dot2_f32_bf16 %5, %10, %13, %19\n\t"
+        "v_dot2_f32_bf16 %6, %11, %12, %20\n\t"
+        "v_dot2_f32_bf16 %7, %11, %13, %21\n\t"
         "s_nop 2"
-        : "=&v"(h0), "=&v"(h1), "=&v"(h2), "=&v"(h3), "=&v"(l0), "=&v"(l1), "=&v"(l2), "=&v"(l3),
-          "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]), "s"(na), "s"(nb));
-    hi = make_uint4(h0, h1, h2, h3);
-    lo = make_uint4(l0, l1, l2, l3);
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "s"(na), "s"(nb),
+          "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ void split8_dot(const float *x, uint4 &hi, uint4 &lo) {
+    const uint32_t h[4] = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+    float r[8];
+    dot_residuals4(h, x, r);
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3]), pack_bf16(r[4], r[5]), pack_bf16(r[6], r[7]));
 }
 
 __device__ __forceinline__ void split4_dot(const float *x, uint2 &hi, uint2 &lo) {
-    uint32_t h0, h1, l0, l1;
-    float r0, r1, r2, r3;
     const uint32_t na = 0x0000bf80u, nb = 0xbf800000u;
+    const uint32_t h0 = pack_bf16(x[0], x[1]), h1 = pack_bf16(x[2], x[3]);
+    float r0, r1, r2, r3;
     asm volatile(
-        "v_cvt_pk_bf16_f32 %0, %8, %9\n\t"
-        "v_cvt_pk_bf16_f32 %1, %10, %11\n\t"
-        "v_dot2_f32_bf16 %4, %0, %12, %8\n\t"
-        "v_dot2_f32_bf16 %5, %0, %13, %9\n\t"
-        "v_dot2_f32_bf16 %6, %1, %12, %10\n\t"
-        "v_dot2_f32_bf16 %7, %1, %13, %11\n\t"
-        "s_nop 1\n\t"
-        "v_cvt_pk_bf16_f32 %2, %4, %5\n\t"
-        "v_cvt_pk_bf16_f32 %3, %6, %7\n\t"
+        "v_dot2_f32_bf16 %0, %4, %6, %8\n\t"
+        "v_dot2_f32_bf16 %1, %4, %7, %9\n\t"
+        "v_dot2_f32_bf16 %2, %5, %6, %10\n\t"
+        "v_dot2_f32_bf16 %3, %5, %7, %11\n\t"
         "s_nop 2"
-        : "=&v"(h0), "=&v"(h1), "=&v"(l0), "=&v"(l1), "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "s"(na), "s"(nb));
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(h0), "v"(h1), "s"(na), "s"(nb), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
     hi = make_uint2(h0, h1);
-    lo = make_uint2(l0, l1);
+    lo = make_uint2(pack_bf16(r0, r1), pack_bf16(r2, r3));
+}
+
+// Two groups of four floats split with one block of dot products.
+__device__ __forceinline__ void split4x2_dot(const float *x, const float *y, uint2 &xh, uint2 &xl, uint2 &yh, uint2 &yl) {
+    const float v[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    uint4 h, l;
+    split8_dot(v, h, l);
+    xh = make_uint2(h.x, h.y);
+    yh = make_uint2(h.z, h.w);
+    xl = make_uint2(l.x, l.y);
+    yl = make_uint2(l.z, l.w);
 }
 
 __device__ __forceinline__ void split8(const float *x, uint4 &hi, uint4 &lo) {

@@ -586,11 +586,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         } else if (HEADG) {
             // k^ and q^ unscaled; the k^ split also fills the transposed Khat^T plane
             const int at = et * OPK + cperm(ec0);
-            uint2 hi, lo;
-            split4_dot(xq, hi, lo);
-            *reinterpret_cast<uint2 *>(QLh + at) = hi;
-            *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = lo;
-            split4_dot(xk, hi, lo);
+            uint2 qhi, qlo, hi, lo;
+            split4x2_dot(xq, xk, qhi, qlo, hi, lo);
+            *reinterpret_cast<uint2 *>(QLh + at) = qhi;
+            *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = qlo;
             *reinterpret_cast<uint2 *>(KLh + at) = hi;
             *reinterpret_cast<uint2 *>(KLh + PL_CD + at) = lo;
             const uint32_t hw[4] = {hi.x, hi.x >> 16, hi.y, hi.y >> 16};
@@ -618,20 +617,18 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             }
             // channels ec0 .. ec0+3 keep their order at channel-permuted position cperm(ec0)
             const int at = et * OPK + cperm(ec0);
-            uint2 hi, lo;
-            split4_dot(kl, hi, lo);
+            uint2 hi, lo, h2, l2;
+            split4x2_dot(kl, krd, hi, lo, h2, l2);
             *reinterpret_cast<uint2 *>(KLh + at) = hi;
             *reinterpret_cast<uint2 *>(KLh + PL_CD + at) = lo;
+            *reinterpret_cast<uint2 *>(KRDh + at) = h2;
+            *reinterpret_cast<uint2 *>(KRDh + PL_CD + at) = l2;
+            // Khat^T[c][t] = k^_t[c] e^{G_C[c] - G_t[c]}; q^ Gamma with it (stored when q is used)
+            split4x2_dot(kht, ql, hi, lo, h2, l2);
             if (qside) {
-                split4_dot(ql, hi, lo);
-                *reinterpret_cast<uint2 *>(QLh + at) = hi;
-                *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = lo;
+                *reinterpret_cast<uint2 *>(QLh + at) = h2;
+                *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = l2;
             }
-            split4_dot(krd, hi, lo);
-            *reinterpret_cast<uint2 *>(KRDh + at) = hi;
-            *reinterpret_cast<uint2 *>(KRDh + PL_CD + at) = lo;
-            // Khat^T[c][t] = k^_t[c] e^{G_C[c] - G_t[c]}
-            split4_dot(kht, hi, lo);
             const uint32_t hw[4] = {hi.x, hi.x >> 16, hi.y, hi.y >> 16};
             const uint32_t lw[4] = {lo.x, lo.x >> 16, lo.y, lo.y >> 16};
 #pragma unroll

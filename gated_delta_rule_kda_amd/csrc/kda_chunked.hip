@@ -29,7 +29,7 @@
 // (the position-pair fallback of that section, taken only where it is needed).
 //
 // Work layout: one workgroup of 8 waves per (sequence, head), walking the
-// sequence's chunks; about 80 KB of LDS and at most 128 VGPRs, so two
+// sequence's chunks; about 69 KB of LDS and at most 128 VGPRs, so two
 // workgroups share a CU (four waves per SIMD) and hide each other's
 // latencies.  Wave w owns value columns 16w .. 16w+15 of S and keeps that
 // 128 x 16 fp32 slice in registers, in the accumulator layout of the 16x16
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     const int nchunks = (L + C - 1) / C;
 
     // Current-row loads of a chunk (q, k, v, log alpha, beta): issued one chunk ahead,
-    // during the previous chunk's state products, so that their latency is hidden.
+    // right after the previous chunk's staging, so that a whole chunk of work hides them.
     typename I4::Raw cur[3];
     typename Vec4<float>::Raw lar;
     float lah = 0.0f;  // head gate: this token's log alpha
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         const int pos = r0 + et;               // this thread's token position
         const bool valid = pos < L;
 
-        // ---- 1. stage this chunk's rows (prefetched during the previous chunk) as fp32 --------
+        // ---- 1. stage this chunk's rows (fetched during the previous chunk) as fp32 -----------
         float xr[3][4];  // this thread's pre-conv values: tap 0 of its convolution
 #pragma unroll
         for (int s = 0; s < 3; ++s) {

@@ -113,14 +113,17 @@ bool scan_supported(const kda_config *cfg) {
 }
 
 // Segment length (tokens, a multiple of the 16-token chunk) and table slots of the
-// segmented prefill: about two segments per compute unit over the N x H items, at
-// least 2048 tokens per segment when the choice is AUTO's (64 when asked for by name).
+// segmented prefill, at least 2048 tokens per segment when the choice is AUTO's (64 when
+// asked for by name).  P segments per sequence rerun P - 1 of them in the last pass; P - 1
+// = floor(2 CUs / items) fills the two workgroup slots of every CU once there, and one
+// more segment would need a second round (131072 tokens: 96 heads, P = 6 took 23.9 ms,
+// P = 5 25.6 and P = 7 29.9; 12 heads, P = 43 took 3.45 ms and P = 42 3.8).
 struct ScanPlan {
     int32_t seg_tokens, slots;
 };
 ScanPlan scan_plan(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens, bool named) {
     const int64_t items = static_cast<int64_t>(num_seqs) * cfg->num_heads;
-    const int64_t per_seq = std::max<int64_t>(2, 2 * device_cu_count() / std::max<int64_t>(items, 1));
+    const int64_t per_seq = std::max<int64_t>(2, 1 + 2 * device_cu_count() / std::max<int64_t>(items, 1));
     const int64_t avg = (total_tokens + num_seqs - 1) / num_seqs;
     int64_t seg = ((avg + per_seq - 1) / per_seq + 15) / 16 * 16;
     seg = std::max<int64_t>(seg, named ? 64 : 2048);

@@ -90,7 +90,8 @@ typedef int32_t kda_status;
  * their outputs.  About 2.6x the arithmetic of one pass, for up to P-fold
  * parallelism: AUTO takes it for bf16 inputs when the (sequence, head) items are
  * fewer than the compute units and sequences average 16384 tokens or more, with
- * about two segments per compute unit.  bf16 io and the LOG_ALPHA, LOWRANK and
+ * P segments per sequence such that the rerun of P - 1 of them fills two workgroup
+ * slots on each compute unit.  bf16 io and the LOG_ALPHA, LOWRANK and
  * HEAD gates only; its M and B matrices live in the workspace. */
 #define KDA_ALGO_CHUNKED_SCAN 5
 

@@ -206,8 +206,9 @@ def test_scan_selection_and_workspace():
     assert kda.resolved_algo(kda.config(96, io_dtype="f32"), 1, 131072) == "recurrent"
     assert kda.resolved_algo(kda.config(96, gate="lowrank_softplus"), 1, 131072) == "chunked_throughput"
     assert kda.resolved_algo(kda.config(96, algo="chunked_throughput"), 1, 131072) == "chunked_throughput"
-    # one 131072-token sequence x 96 heads: 5 segments of 26224 tokens, 6 slots
-    assert kda.workspace_size(c, 1, 131072) == 256 + 256 + 2 * 6 * 96 * 128 * 128 * 4
+    # one 131072-token sequence x 96 heads: 6 segments of 21856 tokens (5 reruns x 96 heads
+    # fill two workgroup slots on each of 256 CUs), 7 slots
+    assert kda.workspace_size(c, 1, 131072) == 256 + 256 + 2 * 7 * 96 * 128 * 128 * 4
     # named: segments of at least 64 tokens (3 x 100 tokens, 2 heads: 3 + 5 slots)
     s = kda.config(2, algo="chunked_scan")
     assert kda.workspace_size(s, 3, 300) == 256 + 256 + 2 * 8 * 2 * 128 * 128 * 4

@@ -436,6 +436,13 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         __syncthreads();
 
         // ---- 2. conv4 + SiLU (+ L2 for q, k) from the staged rows; cumulative log-decay -------
+        // Wave priorities rise through the chunk: staging and the epilogue 0, the convolution 1,
+        // the operands and the products 2, the Gram blocks and T 3, the state update 3.  When
+        // two workgroups share a CU, the one further into its chunk (its matrix-core chains,
+        // short on instructions but long in latency) then issues ahead of the other's
+        // vector-heavy phases, which fill the gaps; with the arbiter's default (older waves
+        // first) one workgroup of the pair ran far behind the other.
+        __builtin_amdgcn_s_setprio(1);
         if (LOWRANK) {
             // log2(alpha) = -5 log2(e) sigmoid(e^{A_h} (z_down W_up^T + b)) for the chunk's
             // tokens (rows) and this wave's 16 channels (columns), on the matrix cores (the
@@ -572,6 +579,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         const bool wide = WIDE && *FLAG != 0;
 
         // ---- 3. staged operands (bf16 hi/lo); the next chunk's conv history ------------------
+        __builtin_amdgcn_s_setprio(2);  // (the order of the phases' priorities: see the convolution)
         if (et >= C - CONV_HIST) {
             // the last three positions become positions -3 .. -1 of the next chunk (the
             // convolution has read the old ones: the barrier above orders it)
@@ -693,11 +701,12 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 if (lrow == 0) VB[u * FPK + lcol] = o;
             }
         } else {
+            __builtin_amdgcn_s_setprio(2);
             // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
             if (wave == 0 || (wave == 1 && qside)) {
                 // the Gram blocks and T gate the next barrier for the whole workgroup: their
                 // waves take issue priority over the other waves of their SIMDs meanwhile
-                __builtin_amdgcn_s_setprio(2);
+                __builtin_amdgcn_s_setprio(3);
                 const uint16_t *Lh = wave == 0 ? KLh : QLh;
                 // two independent accumulation chains (channels 0-63 and 64-127) halve the
                 // dependent-MFMA latency on this critical path
@@ -782,7 +791,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                         PMh[PL_CC + r * OPT + j] = sl;
                     }
                 }
-                __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_s_setprio(2);
             }
             // X = V - Kbar S0 and O1 = Qbar S0.  S0 is the B operand: K step s holds rows
             // 32s + pi(slot), split into bf16 hi/lo right before use.
@@ -843,6 +852,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             __syncthreads();
 
             // ---- 5. U = T X, O = scale (Qbar S + P U), S <- Diag(Gamma_C) S + Khat^T U -------------
+            __builtin_amdgcn_s_setprio(3);  // the chunk's last dependent chain
             {
                 const uint2 Th = *reinterpret_cast<const uint2 *>(TMh + ln * OPT + 4 * lh);
                 const uint2 Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh);
@@ -881,6 +891,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     S[t] = mma(a, (t & 1) ? ul_o : ul_e, S[t]);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);  // the epilogue and the next staging
         }
         __syncthreads();
 

@@ -209,6 +209,13 @@ def test_scan_selection_and_workspace():
     # one 131072-token sequence x 96 heads: 6 segments of 21856 tokens (5 reruns x 96 heads
     # fill two workgroup slots on each of 256 CUs), 7 slots
     assert kda.workspace_size(c, 1, 131072) == 256 + 256 + 2 * 7 * 96 * 128 * 128 * 4
+    # P segments with P - 1 = floor(512 / items): the rerun pass fills two workgroup slots on
+    # each of 256 CUs (12 heads: 43 segments of 3056 tokens, 44 slots; 48 heads: 11 of 11920)
+    for heads, segs in ((12, 43), (48, 11), (32, 17)):
+        seg = -(-(-(-131072 // segs)) // 16) * 16
+        assert (131072 + seg - 1) // seg == segs
+        table = -(-(1 + segs) * 32 // 256) * 256  # one 32-byte descriptor per slot, 256-byte aligned
+        assert kda.workspace_size(kda.config(heads), 1, 131072) == table + 256 + 2 * (1 + segs) * heads * 128 * 128 * 4
     # named: segments of at least 64 tokens (3 x 100 tokens, 2 heads: 3 + 5 slots)
     s = kda.config(2, algo="chunked_scan")
     assert kda.workspace_size(s, 3, 300) == 256 + 256 + 2 * 8 * 2 * 128 * 128 * 4

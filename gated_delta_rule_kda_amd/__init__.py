@@ -26,6 +26,7 @@ F32, BF16 = 0, 1
 ALGOS = {"auto": 0, "recurrent": 1, "chunked": 2, "chunked_throughput": 3, "chunked_latency": 4,
          "chunked_scan": 5}
 GATES = {"log_alpha": 0, "lowrank": 1, "head": 2, "lowrank_softplus": 3, "log_alpha_unbounded": 4}
+BETA_MODES = {"value": 0, "logit": 1}
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 
 EXPORTS = ("kda_config_init", "kda_prefill_workspace_size", "kda_prefill",
@@ -45,7 +46,8 @@ class Config(ctypes.Structure):
                 ("prologue", ctypes.c_int32), ("epilogue", ctypes.c_int32),
                 ("algo", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("gate", ctypes.c_int32), ("gate_rank", ctypes.c_int32)]
+                ("gate", ctypes.c_int32), ("gate_rank", ctypes.c_int32),
+                ("beta_mode", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -121,7 +123,8 @@ def _check(status: int) -> None:
 def config(num_heads: int, io_dtype: str = "bf16", out_dtype: Optional[str] = None,
            prologue: bool = True, epilogue: bool = True, algo: str = "auto",
            scale: Optional[float] = None, l2_eps: float = 1e-6, rms_eps: float = 1e-6,
-           head_dim: int = HEAD_DIM, gate: str = "log_alpha", gate_rank: int = 128) -> Config:
+           head_dim: int = HEAD_DIM, gate: str = "log_alpha", gate_rank: int = 128,
+           beta_mode: str = "value") -> Config:
     c = Config()
     lib().kda_config_init(ctypes.byref(c), num_heads)
     c.head_dim = head_dim
@@ -135,6 +138,7 @@ def config(num_heads: int, io_dtype: str = "bf16", out_dtype: Optional[str] = No
     c.rms_eps = float(rms_eps)
     c.gate = GATES[gate]
     c.gate_rank = int(gate_rank)
+    c.beta_mode = BETA_MODES[beta_mode]
     return c
 
 
@@ -159,6 +163,16 @@ def _stream(stream) -> Optional[int]:
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def _on_stream(stream):
+    """Context in which torch allocates for the launch stream: tensors this binding
+    allocates (outputs, workspace) then belong to the stream the kernels run on, so
+    torch's caching allocator does not hand their memory to other work while the
+    kernels may still use it."""
+    import contextlib
+    import torch
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def _expect(t, name: str, dtype, shape=None) -> None:
@@ -202,7 +216,9 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     gate "lowrank_softplus" takes the same factors and forms Kimi Linear's unbounded
     log alpha = -e^A softplus(z_down W_up^T + b).  With the scalar per-head gate
     (cfg.gate == "head") log_alpha is [T, H] fp32; with "log_alpha_unbounded" it is
-    [T, H, 128] with any value <= 0.
+    [T, H, 128] with any value <= 0.  With beta_mode "logit" beta holds the pre-activation
+    and the kernels apply the sigmoid.  Outputs and the workspace that this function
+    allocates are allocated on `stream` (default: the current stream).
     Returns (o, state_out, conv_out)."""
     import torch
     T, H = q.shape[0], q.shape[1]
@@ -237,18 +253,19 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     _expect(rms_w, "rms_w", torch.float32, (D,))
     _expect(state_in, "state_in", torch.float32, (rows_in, H, D, D))
     dev = q.device
-    if o is None:
-        o = torch.empty((T, H, D), dtype=out_t, device=dev)
+    with _on_stream(stream):
+        if o is None:
+            o = torch.empty((T, H, D), dtype=out_t, device=dev)
+        if state_out is None and return_state and state_out_slots is None:
+            state_out = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+        if conv_out is None and return_conv and cfg.prologue and state_out_slots is None:
+            conv_out = torch.empty((N, 3, 3, H * D), dtype=io_t, device=dev)
+        need = workspace_size(cfg, N, T)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _expect(o, "o", out_t, (T, H, D))
-    if state_out is None and return_state and state_out_slots is None:
-        state_out = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
     _expect(state_out, "state_out", torch.float32, (rows_out, H, D, D))
-    if conv_out is None and return_conv and cfg.prologue and state_out_slots is None:
-        conv_out = torch.empty((N, 3, 3, H * D), dtype=io_t, device=dev)
     _expect(conv_out, "conv_out", io_t, (rows_co, 3, 3, H * D))
-    need = workspace_size(cfg, N, T)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     a = PrefillArgs()
     a.num_seqs, a.cu_seqlens, a.total_tokens = N, _ptr(cu_seqlens), T
     a.q, a.k, a.v, a.log_alpha, a.beta, a.g = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
@@ -303,7 +320,8 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
     if slots_out is not None and slots is None and n_slots < B:
         raise ValueError("state has fewer rows than requests")
     if o is None:
-        o = torch.empty((B, H, D), dtype=out_t, device=q.device)
+        with _on_stream(stream):
+            o = torch.empty((B, H, D), dtype=out_t, device=q.device)
     _expect(o, "o", out_t, (B, H, D))
     a = DecodeArgs()
     a.batch = B

@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
-SOURCES = ["kda_api.hip", "kda_recurrent.hip", "kda_chunked.hip", "kda_chunked_pipe.hip", "kda_scan.hip"]
+SOURCES = ["kda_api.hip", "kda_recurrent.hip", "kda_chunked.hip", "kda_scan.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",

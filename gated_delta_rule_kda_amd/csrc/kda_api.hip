@@ -63,6 +63,7 @@ kda_status check_config(const kda_config *cfg) {
     if (cfg->gate < KDA_GATE_LOG_ALPHA || cfg->gate > KDA_GATE_LOG_ALPHA_UNBOUNDED) return KDA_ERR_INVALID_ARGUMENT;
     if (lowrank_gate(cfg) && (cfg->gate_rank < 32 || cfg->gate_rank > 128 || cfg->gate_rank % 32 != 0))
         return KDA_ERR_UNSUPPORTED;
+    if (cfg->beta_mode != KDA_BETA_VALUE && cfg->beta_mode != KDA_BETA_LOGIT) return KDA_ERR_INVALID_ARGUMENT;
     if (!isfinite(cfg->scale) || !(cfg->l2_eps >= 0.f) || !(cfg->rms_eps >= 0.f) ||
         !isfinite(cfg->l2_eps) || !isfinite(cfg->rms_eps))
         return KDA_ERR_INVALID_ARGUMENT;
@@ -146,6 +147,17 @@ int32_t resolve_algo(const kda_config *cfg, int32_t num_seqs, int64_t total_toke
     return algo;
 }
 
+// Whether the resolved algorithm runs this configuration.  The chunked kernels take bf16
+// io only (their split-bf16 products meet the bf16-input bar, not the fp32 one); the
+// pipelined latency variant is retired; the segmented prefill lacks the per-token path of
+// the gates without a floor; the low-rank gates need bf16 factors on the matrix cores.
+bool supported(const kda_config *cfg, int32_t algo) {
+    if (algo == KDA_ALGO_CHUNKED_LATENCY) return false;
+    if (algo == KDA_ALGO_RECURRENT) return true;
+    if (cfg->io_dtype != KDA_DTYPE_BF16) return false;
+    return algo != KDA_ALGO_CHUNKED_SCAN || scan_supported(cfg);
+}
+
 size_t workspace_bytes(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens, int32_t algo) {
     if (algo != KDA_ALGO_CHUNKED_SCAN) return order_workspace_bytes(num_seqs);
     const ScanPlan sp = scan_plan(cfg, num_seqs, total_tokens, cfg->algo == KDA_ALGO_CHUNKED_SCAN);
@@ -185,11 +197,13 @@ void kda_config_init(kda_config *cfg, int32_t num_heads) {
     cfg->rms_eps = 1e-6f;
     cfg->gate = KDA_GATE_LOG_ALPHA;
     cfg->gate_rank = 128;
+    cfg->beta_mode = KDA_BETA_VALUE;
 }
 
 int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
     if (check_config(cfg) != KDA_OK || num_seqs <= 0 || total_tokens < 0) return -1;
-    return resolve_algo(cfg, num_seqs, total_tokens);
+    const int32_t algo = resolve_algo(cfg, num_seqs, total_tokens);
+    return supported(cfg, algo) ? algo : -1;
 }
 
 kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens,
@@ -220,16 +234,7 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     const int algo = resolve_algo(cfg, a->num_seqs, a->total_tokens);
     const size_t need = workspace_bytes(cfg, a->num_seqs, a->total_tokens, algo);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
-    if (algo == KDA_ALGO_CHUNKED_SCAN && !scan_supported(cfg)) return KDA_ERR_UNSUPPORTED;
-    // the in-kernel low-rank gate runs on the matrix cores with bf16 factors (throughput
-    // variant) or on the VALU (recurrent kernel); the pipelined variant does not have it
-    if (lowrank_gate(cfg) &&
-        (algo == KDA_ALGO_CHUNKED_LATENCY || (algo == KDA_ALGO_CHUNKED_THROUGHPUT && cfg->io_dtype != KDA_DTYPE_BF16)))
-        return KDA_ERR_UNSUPPORTED;
-    // the pipelined variant has neither the head gate nor the per-token path for decays
-    // without a floor
-    if ((cfg->gate == KDA_GATE_HEAD || cfg->gate == KDA_GATE_LOG_ALPHA_UNBOUNDED) && algo == KDA_ALGO_CHUNKED_LATENCY)
-        return KDA_ERR_UNSUPPORTED;
+    if (!supported(cfg, algo)) return KDA_ERR_UNSUPPORTED;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     // the launches below are checked with hipGetLastError: drop an error another call of
@@ -256,6 +261,7 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     p.slots_in = a->state_in_slots; p.slots_out = a->state_out_slots;
     p.scale = cfg->scale; p.l2_eps = cfg->l2_eps; p.rms_eps = cfg->rms_eps;
     p.prologue = cfg->prologue; p.epilogue = cfg->epilogue;
+    p.beta_logit = cfg->beta_mode == KDA_BETA_LOGIT;
     if (trace_enabled())
         fprintf(stderr, "[kda] prefill N=%d H=%d T=%lld io=%d out=%d algo=%d prologue=%d epilogue=%d\n",
                 a->num_seqs, cfg->num_heads, static_cast<long long>(a->total_tokens), cfg->io_dtype,
@@ -266,9 +272,7 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
         if (trace_enabled()) fprintf(stderr, "[kda] scan: %d-token segments, %d slots\n", sp.seg_tokens, sp.slots);
         e = launch_chunked_scan(p, cfg->out_dtype, a->num_seqs, sp.seg_tokens, sp.slots, a->workspace, s);
     } else if (algo == KDA_ALGO_CHUNKED_THROUGHPUT)
-        e = launch_chunked_throughput(p, cfg->io_dtype, cfg->out_dtype, s);
-    else if (algo == KDA_ALGO_CHUNKED_LATENCY)
-        e = launch_chunked_latency(p, cfg->io_dtype, cfg->out_dtype, s);
+        e = launch_chunked_throughput(p, cfg->out_dtype, s);
     else
         e = launch_recurrent(p, cfg->io_dtype, cfg->out_dtype, s);
     return from_hip(e);
@@ -302,6 +306,7 @@ kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *a, void
     p.state_in = a->state; p.state_out = a->state; p.o = a->o;
     p.scale = cfg->scale; p.l2_eps = cfg->l2_eps; p.rms_eps = cfg->rms_eps;
     p.prologue = cfg->prologue; p.epilogue = cfg->epilogue;
+    p.beta_logit = cfg->beta_mode == KDA_BETA_LOGIT;
     if (trace_enabled())
         fprintf(stderr, "[kda] decode B=%d H=%d io=%d out=%d\n", a->batch, cfg->num_heads,
                 cfg->io_dtype, cfg->out_dtype);

@@ -1,5 +1,5 @@
-// kda_chunk_common.h -- operand helpers shared by the chunked prefill kernels
-// (kda_chunked.hip and kda_chunked_pipe.hip): chunk geometry, bf16 hi/lo
+// kda_chunk_common.h -- operand helpers of the chunked prefill kernel
+// (kda_chunked.hip): chunk geometry, bf16 hi/lo
 // operand splits, the gfx950 MFMA wrappers, the K-slot permutation that lets
 // accumulator tiles serve as B operands, and range-checked buffer views.
 #pragma once

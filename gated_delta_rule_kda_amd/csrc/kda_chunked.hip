@@ -1,6 +1,6 @@
-// kda_chunked.hip -- chunked KDA prefill on the gfx950 matrix cores, throughput
-// variant: two workgroups share a CU (for launches with more (sequence, head)
-// items than CUs).  The latency variant is kda_chunked_pipe.hip.
+// kda_chunked.hip -- chunked KDA prefill on the gfx950 matrix cores: two 8-wave
+// workgroups share a CU, one per (sequence, head), or per segment of a sequence in
+// the segmented prefill.  bf16 io.
 //
 // The per-token recurrence of the "Kimi K3 - KDA layer" step list
 // (S <- Diag(alpha) S;  S <- S + beta k (v - S^T k)^T;  o~ = S^T q / sqrt(128))
@@ -35,10 +35,10 @@
 // 128 x 16 fp32 slice in registers, in the accumulator layout of the 16x16
 // MFMAs (lane l holds rows 16t + 4(l/16) + i, column l%16).  Element-wise
 // work maps thread x to token x/32 and four adjacent channels 4(x%32) ..
-// 4(x%32)+3.  Contractions over the 16 tokens of a chunk
-// (v_mfma_f32_16x16x16_bf16) take accumulator tiles directly as their B
-// operand.  Contractions over the 128 key channels (v_mfma_f32_16x16x32_bf16)
-// read S from the same registers: K slot 8h + i of a 32-channel step holds
+// 4(x%32)+3.  Every contraction runs on v_mfma_f32_16x16x32_bf16.  Those over
+// the 16 tokens of a chunk take accumulator tiles directly as their B operand,
+// with a lane's 8 K slots carrying the hi and then the lo parts of its 4 tokens.
+// Those over the 128 key channels read S from the same registers: K slot 8h + i of a 32-channel step holds
 // channel 16(i/4) + 4h + (i%4), so the channel-indexed operands in LDS store
 // their channels in that permuted order (the Gram products contract two such
 // operands, which the permutation leaves unchanged).
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             for (int e = 0; e < 4; ++e) la[e] *= LOG2E;
             store4f(LA + et * D + ec0, la);
         }
-        if ((tid & 31) == 0) BETA[et] = bet;
+        if ((tid & 31) == 0) BETA[et] = p.beta_logit ? sigmoidf_(bet) : bet;
         if (WIDE && tid == 0) *FLAG = 0;
         if (LOWRANK) load_w();  // this lane's W_up operand, used right after the barrier
         // the next chunk's rows: a whole chunk of work hides their latency (past the last
@@ -966,17 +966,17 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     }
 }
 
-template <typename IO, typename OUT>
+template <typename OUT>
 hipError_t launch(const LayerParams &p, hipStream_t s) {
     if (p.num_items == 0) return hipSuccess;
     // log alpha with the floor of -5 never leaves the factorised range; without a floor the
     // chunks past it are found by the vote and take the per-token path
     if (p.gate == KDA_GATE_HEAD)
-        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_HEAD, false, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_HEAD, false, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     else if (p.gate == KDA_GATE_LOG_ALPHA_UNBOUNDED)
-        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_LOG_ALPHA, true, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOG_ALPHA, true, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     else
-        hipLaunchKernelGGL((chunked_tp_kernel<IO, OUT, KDA_GATE_LOG_ALPHA, false, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
+        hipLaunchKernelGGL((chunked_tp_kernel<uint16_t, OUT, KDA_GATE_LOG_ALPHA, false, false>), dim3(p.num_items), dim3(THREADS), 0, s, p);
     return hipGetLastError();
 }
 
@@ -1013,15 +1013,11 @@ hipError_t launch_chunked_segments(const LayerParams &p, int out_dtype, int grid
     return out_dtype == KDA_DTYPE_BF16 ? launch_segments<uint16_t>(p, grid, s) : launch_segments<float>(p, grid, s);
 }
 
-hipError_t launch_chunked_throughput(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s) {
-    if (p.gate == KDA_GATE_LOWRANK || p.gate == KDA_GATE_LOWRANK_SOFTPLUS) {  // bf16 io only (checked by the caller)
-        if (io_dtype != KDA_DTYPE_BF16) return hipErrorInvalidValue;
+// bf16 io only (checked by the caller)
+hipError_t launch_chunked_throughput(const LayerParams &p, int out_dtype, hipStream_t s) {
+    if (p.gate == KDA_GATE_LOWRANK || p.gate == KDA_GATE_LOWRANK_SOFTPLUS)
         return out_dtype == KDA_DTYPE_BF16 ? launch_lowrank<uint16_t>(p, s) : launch_lowrank<float>(p, s);
-    }
-    if (io_dtype == KDA_DTYPE_BF16)
-        return out_dtype == KDA_DTYPE_BF16 ? launch<uint16_t, uint16_t>(p, s)
-                                           : launch<uint16_t, float>(p, s);
-    return out_dtype == KDA_DTYPE_BF16 ? launch<float, uint16_t>(p, s) : launch<float, float>(p, s);
+    return out_dtype == KDA_DTYPE_BF16 ? launch<uint16_t>(p, s) : launch<float>(p, s);
 }
 
 }  // namespace kda

@@ -42,6 +42,7 @@ struct LayerParams {
     void *o;
     float scale, l2_eps, rms_eps;
     int32_t prologue, epilogue;
+    int32_t beta_logit;          // beta holds the pre-activation w: the kernels form sigmoid(w)
     // KDA_GATE_LOWRANK: log alpha = -5 sigmoid(e^{A_h} (z W^T + b)) formed in the kernel;
     // KDA_GATE_LOWRANK_SOFTPLUS: log alpha = -e^{A_h} softplus(z W^T + b)
     int32_t gate, gate_rank;
@@ -59,8 +60,8 @@ struct LayerParams {
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_recurrent(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s);
-hipError_t launch_chunked_throughput(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s);
-hipError_t launch_chunked_latency(const LayerParams &p, int io_dtype, int out_dtype, hipStream_t s);
+// bf16 io only (checked by the caller)
+hipError_t launch_chunked_throughput(const LayerParams &p, int out_dtype, hipStream_t s);
 hipError_t launch_order(const int32_t *cu_seqlens, int32_t n, int32_t *order, hipStream_t s);
 // one pass of the segmented prefill over grid workgroups (bf16 io)
 hipError_t launch_chunked_segments(const LayerParams &p, int out_dtype, int grid, hipStream_t s);

@@ -185,7 +185,10 @@ __global__ __launch_bounds__(THREADS) void recurrent_kernel(LayerParams p) {
                              : p.gate == KDA_GATE_HEAD ? p.log_alpha[static_cast<size_t>(t) * H + h]
                                                        : p.log_alpha[row + c];
             sh_a[buf][c] = __expf(la);
-            if (c == 0) sh_beta[buf] = p.beta[static_cast<size_t>(t) * H + h];
+            if (c == 0) {
+                const float b = p.beta[static_cast<size_t>(t) * H + h];
+                sh_beta[buf] = p.beta_logit ? sigmoidf_(b) : b;  // beta = sigmoid(w) from its pre-activation
+            }
         }
         __syncthreads();
         const float tq = sh_norm[buf][0][0] + sh_norm[buf][1][0];

@@ -42,6 +42,15 @@
  *    reentrant and thread-safe; results are valid once the stream reaches
  *    the call.  Host-side validation failures return an error status and
  *    enqueue nothing.  No call aborts or throws.
+ *  - Initialisation order: the library shares the process's HIP runtime and
+ *    registers its kernels when it is loaded.  Initialise the runtime first
+ *    (any HIP call that touches the device, e.g. hipSetDevice or hipFree(0),
+ *    from the thread that will load the library), then load the library, then
+ *    start other threads that call it.  Loaded into a runtime that was not yet
+ *    initialised while other threads were already running, every later launch
+ *    of the library has been seen to fail with hipErrorNoDevice (KDA_ERR_HIP);
+ *    the cause inside the runtime is not known.  The Python binding follows
+ *    this order (it initialises torch's device before loading the library).
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -54,7 +63,7 @@ extern "C" {
 #endif
 
 #define KDA_HEAD_DIM 128
-#define KDA_ABI_VERSION 4u
+#define KDA_ABI_VERSION 5u
 
 /* Status codes. */
 typedef int32_t kda_status;
@@ -69,22 +78,24 @@ typedef int32_t kda_status;
 #define KDA_DTYPE_BF16 1
 
 /* Prefill algorithm.  AUTO picks CHUNKED for bf16 inputs and RECURRENT for fp32.
- * CHUNKED resolves to the THROUGHPUT variant, the faster one on every launch shape
- * measured (4 x 4096, 1 x 131072 and 64 packed sequences, 96 heads); the LATENCY
- * variant stays selectable by name.  All chunked variants compute in 16-token
- * chunks on the matrix cores with bf16 hi/lo operand splits and fp32
- * accumulation (about 1e-4 relative to an fp64 evaluation); RECURRENT is the
- * fp32 reference-precision path. */
+ * CHUNKED resolves to THROUGHPUT, or to CHUNKED_SCAN for a few long sequences (below).
+ * The chunked algorithms take bf16 io only (fp32 io returns KDA_ERR_UNSUPPORTED): they
+ * compute in 16-token chunks on the matrix cores with bf16 hi/lo operand splits and
+ * fp32 accumulation, which keeps the raw read o~ and the state within about 6e-4 of an
+ * fp64 evaluation (max |err| / RMS), inside the 1e-2 bar of the bf16-input path but
+ * not the 1e-4 bar of the fp32 path.  RECURRENT is the fp32 reference-precision path
+ * (within 1e-4), and takes either io type. */
 #define KDA_ALGO_AUTO 0
 #define KDA_ALGO_RECURRENT 1            /* token-sequential fp32 recurrence */
 #define KDA_ALGO_CHUNKED 2              /* chunked, the variant the library prefers */
 #define KDA_ALGO_CHUNKED_THROUGHPUT 3   /* 8-wave workgroups, two per compute unit */
-#define KDA_ALGO_CHUNKED_LATENCY 4      /* one 8-wave producer/consumer workgroup per compute unit */
+#define KDA_ALGO_CHUNKED_LATENCY 4      /* retired (it was slower at every shape measured):
+                                           returns KDA_ERR_UNSUPPORTED */
 /* CHUNKED_SCAN: the THROUGHPUT kernel over segments of each sequence, run in parallel.
  * A chunk's effect on the state is affine, S -> M S + B (the composition that
  * "Inside Kimi K3 ...", "KDA writes corrections into a recurrent matrix", unrolls
- * token by token), so each segment but the first and last is run twice from S = I
- * with v = 0 (its M) and from S = 0 (its B); the first segment runs from the given
+ * token by token), so each segment but the first and last is run from S = I with
+ * v = 0 (its M) and from S = 0 (its B); the first segment runs from the given
  * state.  A scan S_{p+1} = M_p S_p + B_p over the segments then gives every
  * segment's entering state, and segments 1 .. P-1 run again from it to produce
  * their outputs.  About 2.6x the arithmetic of one pass, for up to P-fold
@@ -106,7 +117,10 @@ typedef int32_t kda_status;
 /* HEAD: one decay per (token, head) shared by the 128 key channels, the scalar gate
  * of Mamba-2 / Gated DeltaNet that KDA generalises ("Kimi K3's Architecture ...",
  * section "Channel-wise decay, and the floor K3 puts under it"): log_alpha is
- * [T][H].  A fast path: the decay factors leave the channel contractions. */
+ * [T][H].  The decay factors leave the channel contractions, so the kernel forms
+ * fewer operand planes; at 4 x 4096 tokens x 96 heads it measured slower than the
+ * channel gate all the same (1.50 against 1.34 ms), since it spends the saved work on
+ * the row scales of the products. */
 #define KDA_GATE_HEAD 2
 /* LOWRANK_SOFTPLUS: Kimi Linear's gate, formed in the kernels from the same factors as
  * LOWRANK: log alpha = -e^{A_h} softplus(z_down W_up^T + b), which has no floor
@@ -116,9 +130,16 @@ typedef int32_t kda_status;
 #define KDA_GATE_LOWRANK_SOFTPLUS 3
 /* LOG_ALPHA_UNBOUNDED: log alpha passed as for LOG_ALPHA but with any value <= 0 (no
  * floor, e.g. a Kimi Linear gate formed outside the library), handled as described for
- * LOWRANK_SOFTPLUS.  On such chunks the per-token decay is taken from differences of
- * running sums, whose fp32 rounding grows with the size of the sums. */
+ * LOWRANK_SOFTPLUS.  On the per-token path each token's decay alpha = exp(log alpha)
+ * is formed from its own log alpha, not from differences of running sums, so a very
+ * deep decay loses no precision. */
 #define KDA_GATE_LOG_ALPHA_UNBOUNDED 4
+
+/* What the beta array holds.  VALUE: beta itself, in [0, 1].  LOGIT: the pre-activation
+ * w = x W_beta of the "Kimi K3 - KDA layer" step list, any finite value; the kernels
+ * form beta = sigmoid(w) themselves. */
+#define KDA_BETA_VALUE 0
+#define KDA_BETA_LOGIT 1
 
 typedef struct {
     int32_t num_heads;   /* H > 0 */
@@ -133,11 +154,12 @@ typedef struct {
     float rms_eps;       /* x / sqrt(mean x^2 + rms_eps) */
     int32_t gate;        /* KDA_GATE_* */
     int32_t gate_rank;   /* r of the LOWRANK gates: a multiple of 32 in [32, 128] */
+    int32_t beta_mode;   /* KDA_BETA_*: what the beta array holds */
 } kda_config;
 
 /* Fills *cfg with the layer's defaults for H heads: bf16 io and output,
  * prologue and epilogue on, AUTO algorithm, scale 1/sqrt(128), eps 1e-6,
- * log alpha given (gate_rank 128 for when LOWRANK is chosen). */
+ * log alpha given (gate_rank 128 for when LOWRANK is chosen), beta given as a value. */
 void kda_config_init(kda_config *cfg, int32_t num_heads);
 
 /* ------------------------------------------------------------------ prefill
@@ -165,7 +187,7 @@ typedef struct {
     const void *q, *k, *v;        /* [T][H][128] io_dtype */
     const float *log_alpha;       /* [T][H][128] fp32 in [-5, 0] (gate LOG_ALPHA) or <= 0 (LOG_ALPHA_UNBOUNDED),
                                      or [T][H] (gate HEAD); else unused */
-    const float *beta;            /* [T][H] fp32, in [0, 1] */
+    const float *beta;            /* [T][H] fp32: beta in [0, 1], or its pre-activation (beta_mode LOGIT) */
     const void *g;                /* [T][H][128] io_dtype; required iff epilogue */
     const float *conv_w;          /* [3][H*128][4] fp32; required iff prologue */
     const void *conv_in;          /* [rows][3][3][H*128] io_dtype or NULL (zero history) */
@@ -203,9 +225,10 @@ int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs, int64
 
 /* -------------------------------------------------------------- decode step
  * One token per request, the same layer core as prefill at T = 1 per
- * sequence: the conv caches are shifted and the state is updated in place
- * ("Kimi K3: Architecture and SGLang Day-0 Support": each step reads and
- * writes only S, which is overwritten in place).  Request b reads pool row
+ * sequence: the conv caches are shifted and the state is updated in place.
+ * A decode step touches only the fixed-size state, no history, and replaces
+ * it where it lies ("Kimi K3: Architecture and SGLang Day-0 Support", the
+ * linear-attention section and "SGLang's day-0 adaptations").  Request b reads pool row
  * slots[b] and writes pool row slots_out[b] (the same row when slots_out is
  * NULL); a distinct out row forks the request from a read-only checkpoint
  * (copy on write).  A row written by one request must not be read or written
@@ -215,7 +238,7 @@ typedef struct {
     int32_t batch;                /* B > 0 requests */
     const void *q, *k, *v;        /* [B][H][128] io_dtype */
     const float *log_alpha;       /* [B][H][128] fp32 (gate LOG_ALPHA) or [B][H] (gate HEAD); else unused */
-    const float *beta;            /* [B][H] fp32 */
+    const float *beta;            /* [B][H] fp32: beta, or its pre-activation (beta_mode LOGIT) */
     const void *g;                /* [B][H][128] io_dtype; required iff epilogue */
     const float *conv_w;          /* [3][H*128][4] fp32; required iff prologue */
     void *conv_state;             /* [slots][3][3][H*128] io_dtype, updated in place; required iff prologue */

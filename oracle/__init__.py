@@ -71,6 +71,19 @@ class Oracle:
         g2.restype = ctypes.c_int
         g2.argtypes = g.argtypes
         self._gate_softplus = g2
+        b = lib.kda_oracle_beta_from_logit
+        b.restype = ctypes.c_int
+        b.argtypes = [ctypes.c_int64, _D, _D]
+        self._beta = b
+
+    def beta_from_logit(self, w):
+        """beta = sigma(w) of the "Kimi K3 - KDA layer" step list, elementwise, from the
+        pre-activation w (any shape)."""
+        w = _f64(w)
+        out = np.zeros_like(w)
+        if self._beta(w.size, _p(w), _p(out)) != 0:
+            raise ValueError("beta_from_logit failed")
+        return out
 
     def lowrank_log_alpha(self, z, w, bias, a):
         """log alpha [T, H, d] of the low-rank gate of the "Kimi K3 - KDA layer" step list,
@@ -242,3 +255,7 @@ def softplus_log_alpha(*args, **kwargs):
 
 def decode_step(*args, **kwargs):
     return default().decode_step(*args, **kwargs)
+
+
+def beta_from_logit(*args, **kwargs):
+    return default().beta_from_logit(*args, **kwargs)

@@ -110,6 +110,15 @@ int kda_oracle_softplus_log_alpha(int64_t T, int H, int d, int r, const double *
     return lowrank_gate(T, H, d, r, z, w, b, a, 1, out);
 }
 
+/* The write strength from its pre-activation ([Atlas] step list: w = x W_beta, then
+ * beta = sigma(w)), one value per (token, head):  beta = 1 / (1 + e^-w).  For w far below
+ * zero e^-w overflows to +inf and beta is 0, the limit. */
+int kda_oracle_beta_from_logit(int64_t n, const double *w, double *beta) {
+    if (n < 0 || (n > 0 && (!w || !beta))) return 1;
+    for (int64_t i = 0; i < n; ++i) beta[i] = 1.0 / (1.0 + exp(-w[i]));
+    return 0;
+}
+
 /* One stream of the prologue for one token ([Atlas] conv + SiLU step):
  * y_c = sum_{j=0..3} w[c][j] * x_{t-j}[c],  a_c = y_c * sigmoid(y_c).
  * hist[0..2] holds x_{t-3}, x_{t-2}, x_{t-1} and is shifted to take x_t. */

@@ -59,7 +59,7 @@ def to_np(t) -> Optional[np.ndarray]:
 def gpu_prefill(inp: Dict[str, np.ndarray], io: str = "bf16", out: str = "f32", algo: str = "auto",
                 prologue: Optional[bool] = None, epilogue: Optional[bool] = None,
                 rms_w: Optional[np.ndarray] = None, in_place: bool = False,
-                keep_device: bool = False, gate: str = "log_alpha"):
+                keep_device: bool = False, gate: str = "log_alpha", beta_mode: str = "value"):
     import torch
     import gated_delta_rule_kda_amd as kda
     io_t = torch.bfloat16 if io == "bf16" else torch.float32
@@ -73,7 +73,7 @@ def gpu_prefill(inp: Dict[str, np.ndarray], io: str = "bf16", out: str = "f32", 
     s0 = to_dev(inp.get("state_in"), torch.float32)
     rw = to_dev(rms_w, torch.float32)
     cfg = kda.config(inp["q"].shape[1], io_dtype=io, out_dtype=out, prologue=prologue,
-                     epilogue=epilogue, algo=algo, gate=gate)
+                     epilogue=epilogue, algo=algo, gate=gate, beta_mode=beta_mode)
     kw = {}
     if in_place and s0 is not None:
         kw["state_out"] = s0

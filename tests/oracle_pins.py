@@ -492,4 +492,26 @@ def pin_softplus_gate_one_hot_channel(orc):
         _close(la, want, 1e-14, f"one-hot channel ({h}, {i})")
 
 
+def pin_beta_logit_closed_forms(orc):
+    """beta = sigma(w) ("Kimi K3 - KDA layer" step list): sigma(0) = 1/2, sigma(ln 3) = 3/4,
+    sigma(-ln 3) = 1/4 exactly up to rounding; the far tails are 0 and 1 with no overflow."""
+    w = np.array([0.0, np.log(3.0), -np.log(3.0), 800.0, -800.0, 40.0])
+    b = orc.beta_from_logit(w)
+    _close(b[:3], np.array([0.5, 0.75, 0.25]), 1e-15, "sigma closed forms")
+    assert b[3] == 1.0 and b[4] == 0.0 and abs(b[5] - 1.0) < 1e-15
+    assert np.all(np.isfinite(b))
+
+
+def pin_beta_logit_symmetry_and_order(orc):
+    """sigma(w) + sigma(-w) = 1, sigma is increasing, and e^{-w} sigma(w) = sigma(-w)
+    (the odds of sigma(w) are e^w) on random pre-activations of any shape."""
+    w = _rng(61).standard_normal((7, 5)) * 4.0
+    b, c = orc.beta_from_logit(w), orc.beta_from_logit(-w)
+    assert b.shape == w.shape
+    _close(b + c, np.ones_like(w), 1e-15, "sigma(w) + sigma(-w)")
+    _close(np.exp(-w) * b, c, 1e-14, "odds of sigma")
+    s = np.sort(w.ravel())
+    assert np.all(np.diff(orc.beta_from_logit(s)) >= 0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

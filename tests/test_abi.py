@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_sizes():
-    assert kda.abi_version() == 4
+    assert kda.abi_version() == 5
     assert kda.state_bytes(96) == 96 * 128 * 128 * 4
     # the pages' per-request figure: 69 KDA layers x 12 heads per GPU at TP=8 x 128^2 x fp32
     assert abs(69 * kda.state_bytes(12) / 1e6 - 54.26) < 0.01
@@ -46,7 +46,28 @@ def test_config_defaults():
     assert (c.num_heads, c.head_dim, c.io_dtype, c.out_dtype, c.prologue, c.epilogue, c.algo) == \
         (96, 128, kda.BF16, kda.BF16, 1, 1, 0)
     assert abs(c.scale - 128 ** -0.5) < 1e-7 and abs(c.l2_eps - 1e-6) < 1e-12
-    assert (c.gate, c.gate_rank) == (0, 128)
+    assert (c.gate, c.gate_rank, c.beta_mode) == (0, 128, 0)
+
+
+def test_config_struct_matches_header():
+    """The Python mirror of kda_config has the header's fields in the header's order."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\} kda_config;", text).group(1)
+    names = re.findall(r"\b(\w+);", body)
+    assert names == [f for f, _ in kda.Config._fields_]
+    assert ctypes.sizeof(kda.Config) == 4 * len(names)
+
+
+def test_beta_mode_validation():
+    """beta_mode LOGIT passes validation (the call below stops at the missing workspace,
+    before any launch); other values are refused."""
+    c = kda.config(4, beta_mode="logit")
+    assert c.beta_mode == 1
+    assert _prefill(c, _args(workspace=None)) == kda.ERR_WORKSPACE_TOO_SMALL
+    bad = kda.config(4)
+    bad.beta_mode = 2
+    assert _prefill(bad, _args(workspace=None)) == kda.ERR_INVALID_ARGUMENT
+    assert kda.lib().kda_prefill_resolved_algo(ctypes.byref(bad), 1, 0) == -1
 
 
 def test_workspace_size():
@@ -158,6 +179,19 @@ def test_lowrank_gate_arguments():
                     _args(**one, **low)) == kda.ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("algo", ["chunked", "chunked_throughput", "chunked_scan", "chunked_latency"])
+@pytest.mark.parametrize("gate", ["log_alpha", "head", "log_alpha_unbounded"])
+def test_chunked_refuses_fp32_io(algo, gate):
+    """The chunked kernels' split-bf16 products meet the bf16-input bar, not the fp32 one:
+    they refuse fp32 io (and the retired latency variant refuses everything), while AUTO
+    sends fp32 io to the recurrent kernel."""
+    one = dict(num_seqs=1, workspace=FAKE, workspace_bytes=1 << 40)
+    c = kda.config(4, io_dtype="f32", algo=algo, gate=gate)
+    assert _prefill(c, _args(**one)) == kda.ERR_UNSUPPORTED
+    assert kda.lib().kda_prefill_resolved_algo(ctypes.byref(c), 1, 64) == -1
+    assert kda.resolved_algo(kda.config(4, io_dtype="f32", gate=gate), 1, 64) == "recurrent"
+
+
 def test_decode_rejects_bad_arguments():
     L = kda.lib()
 
@@ -184,8 +218,9 @@ def test_resolved_algo():
     L = kda.lib()
     c = kda.config(4, io_dtype="f32")
     assert kda.resolved_algo(c, 3) == "recurrent"
-    for name in ("recurrent", "chunked_throughput", "chunked_latency"):
+    for name in ("recurrent", "chunked_throughput"):
         assert kda.resolved_algo(kda.config(4, algo=name), 2) == name
+    assert L.kda_prefill_resolved_algo(ctypes.byref(kda.config(4, algo="chunked_latency")), 2, 0) == -1
     assert kda.resolved_algo(kda.config(8), 1) == "chunked_throughput"
     assert kda.resolved_algo(kda.config(96, algo="chunked"), 4) == "chunked_throughput"
     assert L.kda_prefill_resolved_algo(ctypes.byref(kda.config(4)), 0, 0) == -1
@@ -220,7 +255,6 @@ def test_scan_selection_and_workspace():
     s = kda.config(2, algo="chunked_scan")
     assert kda.workspace_size(s, 3, 300) == 256 + 256 + 2 * 8 * 2 * 128 * 128 * 4
     one = dict(num_seqs=1, workspace=None, workspace_bytes=0)
-    assert _prefill(kda.config(4, algo="chunked_scan", io_dtype="f32"), _args(**one)) == kda.ERR_WORKSPACE_TOO_SMALL
     big = dict(num_seqs=1, workspace=FAKE, workspace_bytes=1 << 40)
     assert _prefill(kda.config(4, algo="chunked_scan", io_dtype="f32"), _args(**big)) == kda.ERR_UNSUPPORTED
     assert _prefill(kda.config(4, algo="chunked_scan", gate="log_alpha_unbounded"), _args(**big)) == kda.ERR_UNSUPPORTED

@@ -5,7 +5,8 @@ Tolerances (max|x - ref| / RMS(ref), per tensor):
   * The chunked kernel's own arithmetic: every contraction uses bf16 hi/lo
     operand splits (three MFMAs, ~2^-16 relative error per product) with
     fp32 accumulation.  Its raw read (no epilogue) stays within 2e-3 of the
-    oracle; the fp32-io reference-precision path is the recurrent kernel.
+    oracle.  The chunked algorithms take bf16 io only; the fp32-io
+    reference-precision path is the recurrent kernel (test_gpu_recurrent.py).
 """
 import numpy as np
 import pytest
@@ -18,8 +19,8 @@ pytestmark = pytest.mark.gpu
 BF16_TOL = 1e-2
 CHUNKED_RAW_TOL = 2e-3
 
-# both chunked kernels: two 4-wave workgroups per CU, and the 8-wave producer/consumer pipeline
-VARIANTS = ["chunked_throughput", "chunked_latency"]
+# the chunked kernel: two 8-wave workgroups per CU
+VARIANTS = ["chunked_throughput"]
 variants = pytest.mark.parametrize("algo", VARIANTS)
 
 
@@ -36,10 +37,13 @@ def _check(g, r, out, tol=BF16_TOL, conv=True):
 
 @variants
 def test_core_recurrence_unit_keys(algo):
-    """B=1, H=2, T=256 core recurrence (fp32 io, no prologue/epilogue) on the chunked path."""
-    inp = W.gen_prefill(W.workload("core_fp32"))
-    say("chunked core_fp32")
-    g = gpu_prefill(inp, io="f32", out="f32", algo=algo)
+    """B=1, H=2, T=256 core recurrence (no prologue/epilogue) on the chunked path, with the
+    core workload's inputs rounded to bf16 (the chunked kernel's io type)."""
+    spec = W.workload("core_fp32")
+    spec.io = "bf16"
+    inp = W.gen_prefill(spec)
+    say("chunked core (bf16 io)")
+    g = gpu_prefill(inp, io="bf16", out="f32", algo=algo)
     r = oracle_prefill(inp)
     _check(g, r, "f32", tol=CHUNKED_RAW_TOL)
 
@@ -100,12 +104,27 @@ def test_in_place_state_and_conv(algo):
 
 
 @variants
-def test_fp32_io_with_gain(algo):
-    spec = W.PrefillSpec(lens=[45, 7], heads=3, io="f32", state_std=0.05, conv_in=True, seed=46)
+def test_random_rms_gain(algo):
+    """A random RMSNorm gain vector (shared by the heads) on the full layer."""
+    spec = W.PrefillSpec(lens=[45, 7], heads=3, state_std=0.05, conv_in=True, seed=46)
     inp = W.gen_prefill(spec)
     rw = np.random.default_rng(5).uniform(0.5, 1.5, 128).astype(np.float32)
-    g = gpu_prefill(inp, io="f32", out="f32", algo=algo, rms_w=rw)
+    g = gpu_prefill(inp, io="bf16", out="f32", algo=algo, rms_w=rw)
     r = oracle_prefill(inp, rms_w=rw)
+    _check(g, r, "f32")
+
+
+@pytest.mark.parametrize("algo", ["chunked_throughput", "chunked_scan"])
+def test_beta_from_logit(algo):
+    """beta passed as its pre-activation w ("Kimi K3 - KDA layer" step list: beta =
+    sigmoid(w)), formed in the kernel; the oracle takes sigmoid(w) from its own fp64 step."""
+    import oracle
+    spec = W.PrefillSpec(lens=[5, 64, 130, 0, 33, 97], heads=3, state_std=0.02, conv_in=True, seed=50)
+    inp = W.gen_prefill(spec)
+    w = (np.random.default_rng(51).standard_normal(inp["beta"].shape) * 2.0).astype(np.float32)
+    say(f"beta from logit ({algo})")
+    g = gpu_prefill(dict(inp, beta=w), io="bf16", out="f32", algo=algo, beta_mode="logit")
+    r = oracle_prefill(dict(inp, beta=oracle.beta_from_logit(w)))
     _check(g, r, "f32")
 
 
@@ -117,14 +136,20 @@ def test_orthonormal_keys_store_all(algo):
     import gated_delta_rule_kda_amd as kda
     from kda_testlib import to_dev
     rng = np.random.default_rng(47)
-    Q, _ = np.linalg.qr(rng.standard_normal((128, 128)))
-    K = Q.T.astype(np.float32)
-    V = rng.standard_normal((128, 128)).astype(np.float32)
+    # orthonormal keys that bf16 holds exactly: 32 diagonal blocks of the 4 x 4 Hadamard
+    # matrix / 2 (entries +-1/2), then a random signed permutation of the channels and of
+    # the key order
+    H4 = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]], np.float64) / 2.0
+    B = np.kron(np.eye(32), H4)
+    B = B[:, rng.permutation(128)] * rng.choice([-1.0, 1.0], 128)[None, :]
+    K = B[rng.permutation(128)].astype(np.float32)
+    assert np.allclose(K @ K.T, np.eye(128), atol=0)
+    V = W.bf16_round(rng.standard_normal((128, 128)).astype(np.float32))
     T = 128
     inp = {"cu_seqlens": np.array([0, T], np.int32), "q": K[:, None, :], "k": K[:, None, :],
            "v": V[:, None, :], "log_alpha": np.zeros((T, 1, 128), np.float32),
            "beta": np.ones((T, 1), np.float32)}
-    g = gpu_prefill(inp, io="f32", out="f32", algo=algo, prologue=False, epilogue=False)
+    g = gpu_prefill(inp, io="bf16", out="f32", algo=algo, prologue=False, epilogue=False)
     S = g["state"][0, 0]
     ref = K.astype(np.float64).T @ V.astype(np.float64)
     e = err(S, ref)
@@ -171,19 +196,25 @@ def test_varlen_subset(algo):
 
 def test_full_size_prefill_sampled():
     """The benchmark's launch (4 x 4096 tokens, 96 heads, bf16 io and output, AUTO
-    algorithm) checked on sampled (sequence, head) pairs against the oracle."""
+    algorithm): all 96 heads of sequence 0 and one head of each other sequence against the
+    oracle, and a second launch bitwise equal to the first (no atomics, fixed orders)."""
+    import torch
     import gated_delta_rule_kda_amd as kda
     spec = W.workload("prefill_4x4096")
     say("prefill_4x4096: generating inputs")
     inp = W.gen_prefill(spec)
-    say("prefill_4x4096: gpu")
-    g = gpu_prefill(inp, io="bf16", out="bf16", algo="auto")
+    say("prefill_4x4096: gpu (twice)")
+    o1, s1, c1 = gpu_prefill(inp, io="bf16", out="bf16", algo="auto", keep_device=True)
+    o2, s2, c2 = gpu_prefill(inp, io="bf16", out="bf16", algo="auto", keep_device=True)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(c1, c2), "prefill is not deterministic"
+    g = dict(o=to_np(o1), state=to_np(s1), conv=to_np(c1))
+    del o1, s1, c1, o2, s2, c2
     assert kda.resolved_algo(kda.config(96), 4, 16384) == "chunked_throughput"
-    for seqs, heads in (([0], [0, 57]), ([3], [95])):
+    for seqs, heads in (([0], list(range(96))), ([1], [17]), ([2], [58]), ([3], [95])):
         sub = subset(inp, seqs, heads)
         r = oracle_prefill(sub)
         gs = gpu_rows(g, inp, seqs, heads)
-        say(f"  seqs {seqs} heads {heads}")
+        say(f"  seqs {seqs} heads {heads if len(heads) < 4 else 'all 96'}")
         _check(gs, r, "bf16")
     # every output is finite
     assert np.isfinite(g["o"]).all() and np.isfinite(g["state"]).all()
@@ -191,17 +222,17 @@ def test_full_size_prefill_sampled():
 
 def test_long_context_sampled():
     """One 131072-token sequence, 96 heads, random fp32 S0 (the long-context launch):
-    sampled heads against the oracle, for the AUTO choice (the segmented prefill), the
-    throughput variant in one sequential pass, and the pipelined variant."""
+    sampled heads against the oracle, for the AUTO choice (the segmented prefill) and the
+    chunked kernel in one sequential pass."""
     import gated_delta_rule_kda_amd as kda
     spec = W.workload("prefill_131072")
     say("prefill_131072: generating inputs")
     inp = W.gen_prefill(spec)
     say("prefill_131072: gpu")
     assert kda.resolved_algo(kda.config(96), 1, 131072) == "chunked_scan"
-    heads = [3, 77]
+    heads = [0, 3, 21, 40, 59, 77, 88, 95]
     r = oracle_prefill(subset(inp, [0], heads))
-    for algo in ("auto", "chunked_throughput", "chunked_latency"):
+    for algo in ("auto", "chunked_throughput"):
         g = gpu_prefill(inp, io="bf16", out="bf16", algo=algo)
         gs = gpu_rows(g, inp, [0], heads)
         say(f"  {algo}: heads {heads}")
@@ -213,7 +244,7 @@ def test_varlen_full_size_sampled():
     """The packed variable-length launch as the benchmark times it: 64 sequences of
     lognormal lengths (578k tokens), 96 heads, per-sequence S0, bf16 io and output, AUTO
     algorithm.  Inputs are generated one sequence at a time straight into device buffers;
-    the longest, a median and the shortest sequence are regenerated on the host and
+    ten sequences, from the longest to the shortest, are regenerated on the host and
     checked on one head each against the oracle."""
     import torch
     import gated_delta_rule_kda_amd as kda
@@ -251,7 +282,8 @@ def test_varlen_full_size_sampled():
     torch.cuda.synchronize()
     del bufs, la, beta
     order = np.argsort(lens)
-    for n, h in ((int(order[-1]), 7), (int(order[N // 2]), 45), (int(order[0]), 90)):
+    picks = [int(order[i]) for i in np.linspace(N - 1, 0, 10).round().astype(int)]
+    for n, h in zip(picks, (7, 45, 90, 3, 66, 12, 31, 80, 54, 95)):
         x = seq(n)
         sub = subset(x, [0], [h])
         r = oracle_prefill(sub)

@@ -40,13 +40,13 @@ def test_head_gate_prefill_ragged(algo, decay):
     assert np.array_equal(g["conv"], r["conv"])
 
 
-def test_head_gate_fp32_io_core():
-    """fp32 io without the prologue and epilogue, on the throughput kernel: the recurrence
-    core alone, over a long sequence with a slow decay that carries S across chunks."""
-    inp = W.gen_prefill(W.PrefillSpec(lens=[400, 17], heads=2, io="f32", prologue=False, epilogue=False,
+def test_head_gate_core():
+    """Without the prologue and epilogue, on the chunked kernel: the recurrence core alone,
+    over a long sequence with a slow decay that carries S across chunks."""
+    inp = W.gen_prefill(W.PrefillSpec(lens=[400, 17], heads=2, prologue=False, epilogue=False,
                                       unit_qk=True, state_std=0.05, decay="slow", seed=83))
     gin, rin = _head(inp)
-    g = gpu_prefill(gin, io="f32", algo="chunked_throughput", gate="head")
+    g = gpu_prefill(gin, io="bf16", algo="chunked_throughput", gate="head")
     r = oracle_prefill(rin)
     assert err(g["o"], r["o"]) <= 1e-2 and err(g["state"], r["state"]) <= 1e-2
 

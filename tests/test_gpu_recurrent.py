@@ -46,6 +46,33 @@ def test_full_layer_recurrent_fp32_io_with_gain():
     assert np.array_equal(g["conv"], r["conv"])
 
 
+def test_beta_from_logit_recurrent_and_decode():
+    """beta given as its pre-activation (sigmoid formed in the kernel), fp32 io, at the fp32
+    bar; then one decode step the same way."""
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    import oracle
+    spec = W.PrefillSpec(lens=[33, 7, 1], heads=3, io="f32", state_std=0.05, conv_in=True, seed=25)
+    inp = W.gen_prefill(spec)
+    w = np.random.default_rng(26).standard_normal(inp["beta"].shape).astype(np.float32) * 3.0
+    g = gpu_prefill(dict(inp, beta=w), io="f32", out="f32", algo="recurrent", beta_mode="logit")
+    r = oracle_prefill(dict(inp, beta=oracle.beta_from_logit(w)))
+    assert err(g["o"], r["o"]) <= FP32_TOL
+    assert err(g["state"], r["state"]) <= FP32_TOL
+    x = _decode_inputs(5, 3, 27)
+    wd = np.random.default_rng(28).standard_normal(x["beta"].shape).astype(np.float32) * 3.0
+    ro, rs, _ = oracle.decode_step(x["q"], x["k"], x["v"], x["log_alpha"], oracle.beta_from_logit(wd),
+                                   x["state"], g=x["g"], conv_w=x["conv_w"], conv_state=x["conv_state"])
+    bf = torch.bfloat16
+    st, cs = to_dev(x["state"], torch.float32), to_dev(x["conv_state"], bf)
+    o = kda.decode_step(to_dev(x["q"], bf), to_dev(x["k"], bf), to_dev(x["v"], bf),
+                        to_dev(x["log_alpha"], torch.float32), to_dev(wd, torch.float32), st,
+                        g=to_dev(x["g"], bf), conv_w=to_dev(x["conv_w"], torch.float32), conv_state=cs,
+                        out_dtype="f32", beta_mode="logit")
+    torch.cuda.synchronize()
+    assert err(to_np(o), ro) <= FP32_TOL and err(to_np(st), rs) <= FP32_TOL
+
+
 def test_edge_lengths_recurrent():
     lens = [0, 1, 3, 15, 16, 17, 63, 64, 65, 0]
     inp = W.gen_prefill(W.PrefillSpec(lens=lens, heads=2, state_std=0.05, conv_in=True, seed=23))
@@ -147,28 +174,32 @@ def test_prefill_then_decode_chain():
     assert np.array_equal(to_np(c), r["conv"])
 
 
-def test_decode_full_size_sampled():
-    """B=256 requests x 96 heads, the launch the benchmark times: sampled
-    (request, head) pairs against the oracle, the conv shift checked everywhere."""
+def test_decode_full_size_all_pairs():
+    """B=256 requests x 96 heads, the launch the benchmark times: every (request, head)
+    pair's output and new state against the oracle's fp64 step, the conv shift checked
+    everywhere, and a second launch from the same inputs bitwise equal to the first."""
     import torch
+    import oracle
     say("decode_256: generating inputs")
     x = W.gen_decode(W.workload("decode_256"))
-    say("decode_256: gpu step")
+    say("decode_256: gpu step (twice)")
     o, st, cs = _gpu_decode(x, out="bf16")
+    o2, st2, cs2 = _gpu_decode(x, out="bf16")
+    assert torch.equal(o, o2) and torch.equal(st, st2) and torch.equal(cs, cs2), "decode is not deterministic"
+    del o2, st2, cs2
     on, stn, csn = to_np(o), to_np(st), to_np(cs)
-    rng = np.random.default_rng(7)
-    reqs = rng.choice(256, 6, replace=False)
-    heads = rng.choice(96, 4, replace=False)
-    import oracle
-    for b in reqs:
-        sl = slice(b, b + 1)
-        ch = np.concatenate([np.arange(h * 128, (h + 1) * 128) for h in heads])
-        ro, rs, rc = oracle.decode_step(x["q"][sl][:, heads], x["k"][sl][:, heads], x["v"][sl][:, heads],
-                                        x["log_alpha"][sl][:, heads], x["beta"][sl][:, heads],
-                                        x["state"][sl][:, heads], g=x["g"][sl][:, heads],
-                                        conv_w=x["conv_w"][:, ch], conv_state=x["conv_state"][sl][..., ch])
-        assert err_bf16(on[sl][:, heads], ro) <= BF16_TOL / 100
-        assert err(stn[sl][:, heads], rs) <= FP32_TOL
+    del st
+    say("decode_256: oracle on all 24576 (request, head) pairs")
+    ro, rs, rc = _oracle_decode(x)
+    eo, es = err_bf16(on, ro), err(stn, rs)
+    say(f"  o err {eo:.2e}  S err {es:.2e}")
+    assert eo <= BF16_TOL / 100
+    assert es <= FP32_TOL
+    # per (request, head) as well: no pair hides behind the global RMS
+    d = np.abs(stn - rs).reshape(256 * 96, -1).max(axis=1)
+    rms = np.sqrt((rs.reshape(256 * 96, -1) ** 2).mean(axis=1))
+    assert (d <= FP32_TOL * np.maximum(rms, 1e-30) * 20).all()
+    assert np.array_equal(csn, rc)
     cin = x["conv_state"].reshape(256, 3, 3, 96 * 128)
     assert np.array_equal(csn[:, :, :2], cin[:, :, 1:])
     newest = np.stack([x["q"], x["k"], x["v"]], axis=1).reshape(256, 3, 96 * 128)

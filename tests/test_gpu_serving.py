@@ -17,7 +17,7 @@ from kda_testlib import err, oracle_prefill, say, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"recurrent": 1e-4, "chunked_throughput": 1e-2, "chunked_latency": 1e-2, "auto": 1e-2}
+TOL = {"recurrent": 1e-4, "chunked_throughput": 1e-2, "auto": 1e-2}
 H = 2
 HD = H * W.D
 
@@ -48,7 +48,7 @@ def _dev_prefill(inp, st_pool, cv_pool, algo, in_slots=None, out_slots=None, wri
     return to_np(o)
 
 
-@pytest.mark.parametrize("algo", ["recurrent", "chunked_throughput", "chunked_latency"])
+@pytest.mark.parametrize("algo", ["recurrent", "chunked_throughput"])
 def test_prefill_reads_and_writes_pool_rows(algo):
     """Three sequences (one of them empty) read pool rows 5, 2, 0 and write rows 1, 6, 3 of
     the same state and conv pools; every other row is left untouched."""

@@ -78,7 +78,7 @@ def _spiky_log_alpha(inp, seed, depth=-300.0):
     return la
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("io", ["bf16"])
 def test_unbounded_log_alpha_spikes(io):
     """log alpha given without a floor: a slow decay (memory of tens of tokens, so S0 and
     the carried state matter) with one-token decays of e^-300 planted in one head."""

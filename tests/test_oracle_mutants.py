@@ -47,6 +47,9 @@ MUTANTS = [
     ("softplus_sign", "u + log1p(exp(-u))", "u - log1p(exp(-u))"),
     ("softplus_naive_overflows", "u > 0.0 ? u + log1p(exp(-u)) : log1p(exp(u))", "log1p(exp(u))"),
     ("softplus_is_sigmoid_branch", "log1p(exp(u)); }", "exp(u); }"),
+    ("beta_logit_sign", "beta[i] = 1.0 / (1.0 + exp(-w[i]));", "beta[i] = 1.0 / (1.0 + exp(w[i]));"),
+    ("beta_logit_identity", "beta[i] = 1.0 / (1.0 + exp(-w[i]));", "beta[i] = w[i];"),
+    ("beta_logit_tanh", "beta[i] = 1.0 / (1.0 + exp(-w[i]));", "beta[i] = 0.5 * (1.0 + tanh(w[i]));"),
 ]
 
 

@@ -29,7 +29,7 @@ GATES = {"log_alpha": 0, "lowrank": 1, "head": 2, "lowrank_softplus": 3, "log_al
 BETA_MODES = {"value": 0, "logit": 1}
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 
-EXPORTS = ("kda_config_init", "kda_prefill_workspace_size", "kda_prefill",
+EXPORTS = ("kda_config_init", "kda_prefill_workspace_size", "kda_prefill", "kda_prefill_no_alloc",
            "kda_prefill_resolved_algo", "kda_decode_step",
            "kda_status_string", "kda_abi_version", "kda_state_bytes")
 
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.kda_prefill_workspace_size.restype = ctypes.c_int32
         L.kda_prefill.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(PrefillArgs), _vp]
         L.kda_prefill.restype = ctypes.c_int32
+        L.kda_prefill_no_alloc.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(PrefillArgs), _vp]
+        L.kda_prefill_no_alloc.restype = ctypes.c_int32
         L.kda_prefill_resolved_algo.argtypes = [ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_int64]
         L.kda_prefill_resolved_algo.restype = ctypes.c_int32
         L.kda_decode_step.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(DecodeArgs), _vp]
@@ -205,7 +207,7 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
             conv_out=None, rms_w=None, state_in=None, state_out=None, o=None, workspace=None,
             state_in_slots=None, state_out_slots=None, gate_z=None, gate_w=None, gate_bias=None,
             gate_a=None, cfg: Optional[Config] = None, return_state: bool = True, return_conv: bool = True,
-            stream=None, **cfg_kwargs) -> Tuple[object, object, object]:
+            stream=None, no_alloc: bool = False, **cfg_kwargs) -> Tuple[object, object, object]:
     """kda_prefill on torch tensors.  q, k, v, g: [T, H, 128]; log_alpha [T, H, 128] fp32;
     beta [T, H] fp32; cu_seqlens int32 [N+1] on the device.  Missing outputs are allocated.
     With state_in_slots / state_out_slots (int32 [N] on the device) the state and conv arrays
@@ -218,7 +220,10 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     (cfg.gate == "head") log_alpha is [T, H] fp32; with "log_alpha_unbounded" it is
     [T, H, 128] with any value <= 0.  With beta_mode "logit" beta holds the pre-activation
     and the kernels apply the sigmoid.  Outputs and the workspace that this function
-    allocates are allocated on `stream` (default: the current stream).
+    allocates are allocated on `stream` (default: the current stream).  With no_alloc the
+    call goes to kda_prefill_no_alloc, which uses the library's static scratch in place of a
+    workspace (pass o, and state_out / conv_out or return_state / return_conv False, for a
+    call that allocates nothing at all).
     Returns (o, state_out, conv_out)."""
     import torch
     T, H = q.shape[0], q.shape[1]
@@ -260,7 +265,7 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
             state_out = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
         if conv_out is None and return_conv and cfg.prologue and state_out_slots is None:
             conv_out = torch.empty((N, 3, 3, H * D), dtype=io_t, device=dev)
-        need = workspace_size(cfg, N, T)
+        need = 0 if no_alloc else workspace_size(cfg, N, T)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _expect(o, "o", out_t, (T, H, D))
@@ -276,7 +281,8 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.state_in_slots, a.state_out_slots = _ptr(state_in_slots), _ptr(state_out_slots)
     a.gate_z, a.gate_w, a.gate_bias, a.gate_a = _ptr(gate_z), _ptr(gate_w), _ptr(gate_bias), _ptr(gate_a)
-    _check(lib().kda_prefill(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
+    fn = lib().kda_prefill_no_alloc if no_alloc else lib().kda_prefill
+    _check(fn(ctypes.byref(cfg), ctypes.byref(a), _stream(stream)))
     return o, state_out, conv_out
 
 

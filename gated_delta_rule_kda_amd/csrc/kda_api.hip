@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kda_internal.h"
 
@@ -215,7 +216,14 @@ kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs, i
     return KDA_OK;
 }
 
-kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Host validation shared by both prefill entry points: everything but the workspace.
+// On success *algo is the algorithm that will run and *need the workspace bytes it uses.
+kda_status check_prefill(const kda_config *cfg, const kda_prefill_args *a, const void *workspace, int32_t *algo,
+                         size_t *need) {
     kda_status st = check_config(cfg);
     if (st != KDA_OK) return st;
     if (!a || a->num_seqs <= 0 || a->total_tokens < 0) return KDA_ERR_INVALID_ARGUMENT;
@@ -228,19 +236,32 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
         !ok_ptr(a->o, tok) || !ok_ptr(a->g, tok && cfg->epilogue) ||
         !ok_ptr(a->conv_w, cfg->prologue != 0) || !ok_ptr(a->conv_in, false) ||
         !ok_ptr(a->conv_out, false) || !ok_ptr(a->rms_w, false) || !ok_ptr(a->state_in, false) ||
-        !ok_ptr(a->state_out, false) || !ok_ptr(a->workspace, false) ||
+        !ok_ptr(a->state_out, false) || !ok_ptr(workspace, false) ||
         !ok_ptr(a->state_in_slots, false) || !ok_ptr(a->state_out_slots, false))
         return KDA_ERR_INVALID_ARGUMENT;
-    const int algo = resolve_algo(cfg, a->num_seqs, a->total_tokens);
-    const size_t need = workspace_bytes(cfg, a->num_seqs, a->total_tokens, algo);
-    if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    *algo = resolve_algo(cfg, a->num_seqs, a->total_tokens);
+    *need = workspace_bytes(cfg, a->num_seqs, a->total_tokens, *algo);
+    return KDA_OK;
+}
+
+// A validated prefill call and its launches, with the workspace given apart from the
+// arguments (the caller's, or the library's static scratch): a workspace smaller than the
+// resolved algorithm needs (or NULL where one is needed) is refused, then a configuration
+// the algorithm does not run, and only then is anything enqueued.
+kda_status prefill_with(const kda_config *cfg, const kda_prefill_args *a, void *hip_stream, void *workspace,
+                        size_t ws_bytes) {
+    int32_t algo = 0;
+    size_t need = 0;
+    kda_status st = check_prefill(cfg, a, workspace, &algo, &need);
+    if (st != KDA_OK) return st;
+    if (need > 0 && (!workspace || ws_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (!supported(cfg, algo)) return KDA_ERR_UNSUPPORTED;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     // the launches below are checked with hipGetLastError: drop an error another call of
     // this thread left recorded in the (process-wide) runtime
     (void)hipGetLastError();
-    int32_t *order = need > 0 && algo != KDA_ALGO_CHUNKED_SCAN ? static_cast<int32_t *>(a->workspace) : nullptr;
+    int32_t *order = need > 0 && algo != KDA_ALGO_CHUNKED_SCAN ? static_cast<int32_t *>(workspace) : nullptr;
     if (order) {
         st = from_hip(launch_order(a->cu_seqlens, a->num_seqs, order, s));
         if (st != KDA_OK) return st;
@@ -270,12 +291,63 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *h
     if (algo == KDA_ALGO_CHUNKED_SCAN) {
         const ScanPlan sp = scan_plan(cfg, a->num_seqs, a->total_tokens, cfg->algo == KDA_ALGO_CHUNKED_SCAN);
         if (trace_enabled()) fprintf(stderr, "[kda] scan: %d-token segments, %d slots\n", sp.seg_tokens, sp.slots);
-        e = launch_chunked_scan(p, cfg->out_dtype, a->num_seqs, sp.seg_tokens, sp.slots, a->workspace, s);
+        e = launch_chunked_scan(p, cfg->out_dtype, a->num_seqs, sp.seg_tokens, sp.slots, workspace, s);
     } else if (algo == KDA_ALGO_CHUNKED_THROUGHPUT)
         e = launch_chunked_throughput(p, cfg->out_dtype, s);
     else
         e = launch_recurrent(p, cfg->io_dtype, cfg->out_dtype, s);
     return from_hip(e);
+}
+
+// Scratch of kda_prefill_no_alloc: one static array per GPU, held for the life of the
+// process.  In host code `scratch` names a host-side stand-in, not the device array, so
+// host code uses only the per-device address looked up below.
+__device__ __align__(256) unsigned char scratch[KDA_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 256;
+std::mutex scratch_mu;
+void *scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// Device address of `scratch` on the device of `s` (the current device for the null
+// stream), looked up once per device with that device current.
+kda_status device_scratch(hipStream_t s, void **out) {
+    int cur = -1, dev = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return KDA_ERR_HIP;
+    dev = cur;
+    if (s && hipStreamGetDevice(s, &dev) != hipSuccess) return KDA_ERR_HIP;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return KDA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return KDA_ERR_HIP;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) return KDA_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *hip_stream) {
+    return prefill_with(cfg, a, hip_stream, a ? a->workspace : nullptr, a ? a->workspace_bytes : 0);
+}
+
+kda_status kda_prefill_no_alloc(const kda_config *cfg, const kda_prefill_args *a, void *hip_stream) {
+    int32_t algo = 0;
+    size_t need = 0;
+    kda_status st = check_prefill(cfg, a, nullptr, &algo, &need);
+    if (st != KDA_OK) return st;
+    if (need > KDA_NO_ALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
+    if (!supported(cfg, algo)) return KDA_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    st = device_scratch(static_cast<hipStream_t>(hip_stream), &ws);
+    if (st != KDA_OK) return st;
+    return prefill_with(cfg, a, hip_stream, ws, KDA_NO_ALLOC_SCRATCH_BYTES);
 }
 
 kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *a, void *hip_stream) {

@@ -217,6 +217,26 @@ kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
 
 kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *args, void *hip_stream);
 
+/* kda_prefill for callers that cannot allocate device memory: code being captured into a
+ * HIP graph, tight serving loops, and harnesses that forbid allocation.  The arguments are
+ * those of kda_prefill except that args->workspace and args->workspace_bytes are ignored:
+ * the library's own static scratch of KDA_NO_ALLOC_SCRATCH_BYTES per GPU takes their
+ * place.  That array is a file-scope device array, one per GPU the library runs on, held
+ * until the process ends; no call here allocates or frees memory.  Limit: configurations
+ * whose workspace (kda_prefill_workspace_size) exceeds KDA_NO_ALLOC_SCRATCH_BYTES return
+ * KDA_ERR_WORKSPACE_TOO_SMALL and enqueue nothing: the segmented prefill
+ * (KDA_ALGO_CHUNKED_SCAN) never fits, so choose KDA_ALGO_CHUNKED_THROUGHPUT or call
+ * kda_prefill with a workspace for a few very long sequences; the other algorithms need
+ * at most 32 KiB (the longest-first order of up to 8192 sequences).  Every call on one
+ * GPU shares that GPU's array, and the kernels overwrite all of it that they read, so no
+ * state carries from one call to the next; calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race on the array and
+ * must not be made.  The first call on a GPU looks up the array's device address
+ * (hipGetSymbolAddress, with that GPU made current for the lookup); a failure there
+ * returns KDA_ERR_HIP. */
+#define KDA_NO_ALLOC_SCRATCH_BYTES 65536u
+kda_status kda_prefill_no_alloc(const kda_config *cfg, const kda_prefill_args *args, void *hip_stream);
+
 /* The KDA_ALGO_* that kda_prefill runs for this configuration, num_seqs sequences
  * and total_tokens tokens on the current device (AUTO and CHUNKED resolved), or -1
  * when the configuration is invalid, num_seqs <= 0 or total_tokens < 0.  Host only;

@@ -212,6 +212,24 @@ def test_decode_rejects_bad_arguments():
     assert dec(kda.config(4, head_dim=256)) == kda.ERR_UNSUPPORTED
 
 
+def test_no_alloc_validation():
+    """kda_prefill_no_alloc validates like kda_prefill and ignores the caller's workspace;
+    a configuration whose workspace exceeds the static scratch (the segmented prefill) is
+    refused before any HIP call."""
+    L = kda.lib()
+
+    def na(cfg, a):
+        return L.kda_prefill_no_alloc(ctypes.byref(cfg), ctypes.byref(a), None)
+
+    big = dict(num_seqs=1, total_tokens=131072, workspace=None, workspace_bytes=0)
+    assert na(kda.config(96), _args(**big)) == kda.ERR_WORKSPACE_TOO_SMALL  # AUTO -> scan
+    assert na(kda.config(4, algo="chunked_scan"), _args(num_seqs=3, total_tokens=300)) == kda.ERR_WORKSPACE_TOO_SMALL
+    assert na(kda.config(4), _args(q=None)) == kda.ERR_INVALID_ARGUMENT
+    assert na(kda.config(4), _args(num_seqs=0)) == kda.ERR_INVALID_ARGUMENT
+    assert na(kda.config(4, head_dim=64), _args()) == kda.ERR_UNSUPPORTED
+    assert na(kda.config(4, io_dtype="f32", algo="chunked_throughput"), _args(num_seqs=1)) == kda.ERR_UNSUPPORTED
+
+
 def test_resolved_algo():
     # fp32 io -> the recurrent reference path; explicit choices pass through;
     # invalid configurations and sequence counts -> -1

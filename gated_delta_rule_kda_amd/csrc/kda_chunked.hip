@@ -13,7 +13,8 @@
 //   T       = (I + A)^{-1} Diag(beta)
 //   U       = T (V - Kbar S0),            Kbar = Gamma (.) K
 //   O       = scale (Qbar S0 + P U),      Qbar = Gamma (.) Q
-//   S1      = Diag(Gamma_C) S0 + Khat^T U, Khat = e^{G_C - G} (.) K
+//   S1      = Diag(Gamma_C) (S0 + Kdiv^T U),  Kdiv = e^{-G} (.) K
+//           ( = Diag(Gamma_C) S0 + Khat^T U with Khat = e^{G_C - G} (.) K )
 //
 // which is the recurrence unrolled over the chunk: u_r = beta_r (v_r -
 // (Diag(alpha_r) S_{r-1})^T k_r) is the per-token correction, and stacking
@@ -59,8 +60,8 @@ constexpr int THREADS = NW * 64;
 
 // ------------------------------------------------------------------ LDS map (bytes)
 
-// Khat^T plane: row c holds the 16 hi parts of the chunk's tokens, then the 16 lo parts,
-// then 4 padding elements (KHTR = 36 bf16), so one 16-byte pair of reads fetches both
+// Kdiv^T plane (the head gate's K^T): row c holds the 16 hi parts of the chunk's tokens,
+// then the 16 lo parts, then 4 padding elements (KHTR = 36 bf16), so one 16-byte pair of reads fetches both
 // parts of a 4-token group.  Token t sits at t XOR 2 ((c / 16) % 8) inside each part:
 // every aligned group of four tokens stays contiguous (the MFMA operand reads; odd
 // c / 16 swaps the group's two halves), and both the transposing 16-bit stores (32
@@ -73,19 +74,21 @@ __device__ __forceinline__ int kht_pos(int c, int t) { return c * KHTR + (t ^ (2
 // positions -3 .. 15 of the chunk: the three history rows come first, so the four
 // taps of a token are four fixed offsets from one address.  The history rows persist
 // from chunk to chunk; the chunk's own rows are dead once the convolution has read
-// them, and share their bytes with the K / Q / Khat operand planes written after it.
+// them, and share their bytes with the K / Q / Kdiv operand planes written after it.
 constexpr int RAW_ROW = 3 * D * 4;                   // one token position, three streams
 constexpr int OFF_HIST = 0;                          // positions -3 .. -1
 constexpr int OFF_CUR = OFF_HIST + CONV_HIST * RAW_ROW;  // positions 0 .. 15
 constexpr int OFF_KL = OFF_CUR;                      // k^ Gamma (= Kbar), channel-permuted      hi,lo
 constexpr int OFF_QL = OFF_KL + 2 * PL_CD * 2;       // q^ Gamma (= Qbar), channel-permuted      hi,lo
-constexpr int OFF_KHT = OFF_QL + 2 * PL_CD * 2;      // Khat^T [channel][hi 16 | lo 16 | pad]   swizzled
-constexpr int OFF_KRD = OFF_KHT + D * KHTR * 2;      // k^ / Gamma, channel-permuted             hi,lo
-constexpr int OFF_O = OFF_KRD;                       // fp32 [16][132] output staging (after the Gram)
-constexpr int OFF_V = OFF_KRD + 2 * PL_CD * 2;       // fp32 [16][132]
+constexpr int OFF_KRD = OFF_QL + 2 * PL_CD * 2;      // k^ / Gamma (= Kdiv), channel-permuted    hi,lo
+constexpr int OFF_KHT = OFF_KRD + 2 * PL_CD * 2;     // Kdiv^T [channel][hi 16 | lo 16 | pad]   swizzled
+constexpr int OFF_V = OFF_KHT + D * KHTR * 2;        // fp32 [16][132]
 constexpr int OFF_LA = OFF_V + C * FPK * 4;          // log2(alpha) -> cumulative, fp32 [16][128]
-constexpr int AFK = 20;                              // row of the A staging (k-major)
-constexpr int OFF_AF = OFF_LA + C * D * 4;           // A (beta-scaled) fp32 [16][4][4], rows of AFK
+// fp32 [16][132] output rows of a chunk: written at its state update, read by its epilogue
+// during the next chunk's Gram / T phase
+constexpr int OFF_O = OFF_LA + C * D * 4;
+constexpr int AFK = 16;                              // row of the A staging (k-major)
+constexpr int OFF_AF = OFF_O + C * FPK * 4;          // A (beta-scaled) fp32 [16][4][4], rows of AFK
 constexpr int OFF_PM = OFF_AF + C * AFK * 4;         // P                                        hi,lo [16][20]
 constexpr int OFF_TM = OFF_PM + 2 * PL_CC * 2;       // T                                        hi,lo [16][20]
 constexpr int OFF_BETA = OFF_TM + 2 * PL_CC * 2;     // fp32 [16]
@@ -100,21 +103,22 @@ constexpr int OFF_ZL = LDS_BYTES;
 constexpr int LDS_BYTES_LOWRANK = OFF_ZL + C * ZPK * 2;
 
 // Per-token path of a chunk whose decay leaves the factorised range: fp32 k^ and q^ rows
-// [16][FPK] in the K / Q planes; alpha [16][128] in the k^ / Gamma plane, written with the
+// [16][FPK] in the K / Q planes; alpha [16][128] in the Kdiv^T plane, written with the
 // running sums (that plane is free from the first barrier of a chunk until the operands
-// are built); the V rows, which each token's outputs overwrite once they are read.  The
-// vote flag shares the head-gate slot.
+// are built, and a chunk on this path builds no Kdiv^T; the planes before it hold the
+// staged rows that the convolution is still reading then); the V rows; outputs go to the
+// output rows as on the matrix-core path.  The vote flag shares the head-gate slot.
 constexpr int OFF_KF = OFF_KL;
 constexpr int OFF_QF = OFF_KF + C * FPK * 4;
-constexpr int OFF_AL = OFF_KRD;
+constexpr int OFF_AL = OFF_KHT;
 constexpr int OFF_FLAG = OFF_GH;
 // a chunk keeps the factorised path while every channel's decay over it stays above
 // 2^-WIDE_LOG2: e^{-G} <= 2^116 then, and the lo parts of e^{G} k^ stay normal in bf16
 constexpr float WIDE_LOG2 = 116.0f;
-static_assert(OFF_QF + C * FPK * 4 <= OFF_KHT, "fp32 k^ and q^ rows must fit in the K / Q planes");
-static_assert(C * D * 4 <= 2 * PL_CD * 2, "alpha must fit in the k^ / Gamma plane");
-static_assert(C * RAW_ROW <= OFF_KRD - OFF_CUR, "staged rows must fit under the K / Q / Khat planes");
-static_assert(C * FPK * 4 <= 2 * PL_CD * 2, "output staging must fit in the KRD slot");
+static_assert(OFF_QF + C * FPK * 4 <= OFF_KRD, "fp32 k^ and q^ rows must fit in the K / Q planes");
+static_assert(C * D * 4 <= D * KHTR * 2, "alpha must fit in the Kdiv^T plane");
+static_assert(OFF_AL >= OFF_CUR + C * RAW_ROW, "alpha, written during the convolution, must not overlap the staged rows");
+static_assert(C * RAW_ROW <= OFF_KHT - OFF_CUR, "staged rows must fit under the K / Q / Kdiv planes");
 static_assert(2 * LDS_BYTES_LOWRANK <= 160 * 1024, "two workgroups per gfx950 CU");
 
 constexpr float LOG2E = 1.4426950408889634f;
@@ -229,7 +233,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     const size_t hD = static_cast<size_t>(h) * D;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    // the wave index is the same in every lane of a wave: read it into a scalar, so that the
+    // per-wave roles below branch on scalars and their buffer views need no lane reads
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int ln = lane & 15;        // MFMA row / column index
     const int lh = lane >> 4;        // MFMA K group
@@ -292,7 +298,6 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     typename Vec4<float>::Raw lar;
     float lah = 0.0f;  // head gate: this token's log alpha
     float bet = 0.0f;
-    typename I4::Raw graw;
     // byte addresses of this (sequence, head)'s first row in each token-major tensor; a
     // chunk's rows start C rows further per chunk, and offsets inside a chunk fit 32 bits
     const uint32_t rowb_io = static_cast<uint32_t>(HD * sizeof(IO));
@@ -360,17 +365,73 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             wb[st] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     };
-    // Issued on every path, past the last chunk too (an empty view reads zeros without a
-    // memory access), so that the wait for a chunk's rows always counts the same younger
-    // memory operations and never has to wait for the output stores as well.
-    auto load_gate = [&](int c) {
-        const int x = opaque(tid);
+    // The epilogue of a chunk runs on waves 4-7 during the next chunk's Gram / T phase, where
+    // they would otherwise wait for the triangular solve of wave 0: thread x = tid - 256 takes
+    // token x / 16 and channels 8 (x % 16) .. + 7, so a token's 128 channels form one 16-lane
+    // row and its RMS sum takes four DPP steps.  Every wave issues the same memory operations
+    // in the same order whether or not it has outputs (views without bytes are dropped without
+    // a memory access), so that the wait for a chunk's rows always counts the same younger
+    // operations and never has to wait for an output store as well.
+    constexpr int EPI_WAVE = 4;
+    const bool epi_wave = wave >= EPI_WAVE;
+    const bool do_epi = !SEG || has_out;
+    typename Vec8<IO>::Raw graw;
+    // g rows of chunk c for the epilogue threads (use = false: an empty load in their place)
+    auto load_gate = [&](int c, bool use) {
+        const int x = opaque(tid) - EPI_WAVE * 64;
+        use = use && p.epilogue && do_epi && epi_wave;
         const int r0 = c * C;
-        const bool use = p.epilogue && has_out;
         const int nrow = use ? min(L, r0 + C) - r0 : 0;
         const char *const gb = use ? g_base + static_cast<size_t>(r0) * rowb_io : static_cast<const char *>(p.q);
-        graw = IB::load(rows_view(gb, nrow, rowb_io, D * sizeof(IO)),
-                        static_cast<uint32_t>(x >> 5) * rowb_io + (x & 31) * 4 * sizeof(IO));
+        graw = BufLoad8<IO>::load(rows_view(gb, nrow, rowb_io, D * sizeof(IO)),
+                                  use ? static_cast<uint32_t>(x >> 4) * rowb_io + (x & 15) * 8 * sizeof(IO) : 0u);
+    };
+    // the memory operations of an epilogue's output store, dropped
+    auto store_dummy = [&]() {
+        const __amdgpu_buffer_rsrc_t none = rows_view(o_base, 0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0u, 0, 0);
+        if (sizeof(OUT) == 4) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0u, 0, 0);
+    };
+    // sigma(g) * RMSNorm(o~) * w of chunk c from its output rows (waves 4-7 only)
+    auto epilogue = [&](int c) {
+        const int x = opaque(tid) - EPI_WAVE * 64, xt = x >> 4, xc = (x & 15) * 8;
+        const int r0 = c * C, nrow = min(L, r0 + C) - r0;
+        float o[8];
+        load4f(OB + xt * FPK + xc, o);
+        load4f(OB + xt * FPK + xc + 4, o + 4);
+        if (p.epilogue) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(o[e], o[e], ss);
+            ss += dpp<0xB1>(ss);   // quad_perm [1, 0, 3, 2]
+            ss += dpp<0x4E>(ss);   // quad_perm [2, 3, 0, 1]
+            ss += dpp<0x141>(ss);  // row_half_mirror
+            ss += dpp<0x140>(ss);  // row_mirror: the sum over the 16-lane row
+            const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.rms_eps);
+            float g[8], rw[8];
+            Vec8<IO>::unpack(graw, g);
+            load4f(RW + xc, rw);
+            load4f(RW + xc + 4, rw + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = sigmoidf_(g[e]) * (o[e] * inv) * rw[e];
+        }
+        OutStore<OUT>::store(rows_view(o_base + static_cast<size_t>(r0) * HD * sizeof(OUT), nrow,
+                                       static_cast<uint32_t>(HD * sizeof(OUT)), D * sizeof(OUT)),
+                             static_cast<uint32_t>(xt) * static_cast<uint32_t>(HD * sizeof(OUT)) + xc * sizeof(OUT), o);
+    };
+    // At the start of chunk ch's Gram / T phase: the outputs of chunk ch - 1 (or the same
+    // memory operations, dropped).  At the end of its state update: the g rows of chunk ch
+    // and the low-rank gate's z_down rows of chunk ch + 1, so that neither is held in
+    // registers through the triangular solve and the state products.
+    auto epilogue_stage = [&](int ch) {
+        if (epi_wave && do_epi && ch > 0)
+            epilogue(ch - 1);
+        else
+            store_dummy();
+    };
+    auto next_loads = [&](int ch) {
+        load_gate(ch, true);
+        if (LOWRANK) load_z(ch + 1);
     };
     if (p.prologue && tid < 3 * CONV_HIST * 16) {
         // history of the first chunk: the given conv cache (oldest first) or zeros
@@ -388,12 +449,11 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 
     if (nchunks > 0) {
         load_current(0);
-        // an empty store (its view has no bytes, so it is dropped without a memory access)
-        // where the loop has the previous chunk's output store: the same memory operations
-        // then follow a chunk's rows on both ways into the loop, and the wait for the rows
-        // at the top of the loop need not cover the output store
-        __builtin_amdgcn_raw_buffer_store_b32(0u, rows_view(o_base, 0, 0, 0), 0u, 0, 0);
-        load_gate(0);
+        // the memory operations of an epilogue stage (an empty store and an empty g load):
+        // the same operations then follow a chunk's rows on both ways into the loop, and the
+        // wait for the rows at the top of the loop need not cover the output store
+        store_dummy();
+        load_gate(0, false);
         if (LOWRANK) {
             load_z(0);
             load_w();
@@ -418,7 +478,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         if (LOWRANK) {
             park_z();  // ZL was last read before the previous chunk's second barrier
         } else if (HEADG) {
-            if ((tid & 31) == 0) GH[et] = lah * LOG2E;
+            if ((tid & 31) == 0) GH[opaque(tid) >> 5] = lah * LOG2E;
         } else {
             float la[4];
             Vec4<float>::unpack(lar, la);
@@ -426,7 +486,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             for (int e = 0; e < 4; ++e) la[e] *= LOG2E;
             store4f(LA + et * D + ec0, la);
         }
-        if ((tid & 31) == 0) BETA[et] = p.beta_logit ? sigmoidf_(bet) : bet;
+        // (the address from an opaque thread index: a spilled address costs a reload that waits
+        // for every memory operation in flight)
+        if ((tid & 31) == 0) BETA[opaque(tid) >> 5] = p.beta_logit ? sigmoidf_(bet) : bet;
         if (WIDE && tid == 0) *FLAG = 0;
         if (LOWRANK) load_w();  // this lane's W_up operand, used right after the barrier
         // the next chunk's rows: a whole chunk of work hides their latency (past the last
@@ -540,7 +602,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     xq[e] *= iq;
                     xk[e] *= ik;
                 }
-                if (!valid) {  // padding tokens past the end see real history rows: clear them
+                // padding tokens past the end of a partial chunk see real history rows: clear
+                // them (a branch on the chunk, the same in every thread, skips this for full ones)
+                if (rend - r0 < C && !valid) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) xq[e] = xk[e] = xv[e] = 0.0f;
                 }
@@ -592,7 +656,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             store4f(QF + et * FPK + ec0, xq);
             store4f(VB + et * FPK + ec0, xv);
         } else if (HEADG) {
-            // k^ and q^ unscaled; the k^ split also fills the transposed Khat^T plane
+            // k^ and q^ unscaled; the k^ split also fills the transposed K^T plane
             const int at = et * OPK + cperm(ec0);
             uint2 qhi, qlo, hi, lo;
             split4x2_dot(xq, xk, qhi, qlo, hi, lo);
@@ -610,10 +674,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             }
             store4f(VB + et * FPK + ec0, xv);
         } else {
-            float gl[4], egc[4];
+            float gl[4];
             load4f(LA + et * D + ec0, gl);
-            load4f(EGC + ec0, egc);
-            float kl[4], ql[4], krd[4], kht[4];
+            float kl[4], ql[4], krd[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float E = __builtin_amdgcn_exp2f(gl[e]);
@@ -621,7 +684,6 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 kl[e] = xk[e] * E;
                 ql[e] = xq[e] * E;
                 krd[e] = xk[e] * rE;
-                kht[e] = krd[e] * egc[e];
             }
             // channels ec0 .. ec0+3 keep their order at channel-permuted position cperm(ec0)
             const int at = et * OPK + cperm(ec0);
@@ -631,14 +693,14 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             *reinterpret_cast<uint2 *>(KLh + PL_CD + at) = lo;
             *reinterpret_cast<uint2 *>(KRDh + at) = h2;
             *reinterpret_cast<uint2 *>(KRDh + PL_CD + at) = l2;
-            // Khat^T[c][t] = k^_t[c] e^{G_C[c] - G_t[c]}; q^ Gamma with it (stored when q is used)
-            split4x2_dot(kht, ql, hi, lo, h2, l2);
-            if (qside) {
-                *reinterpret_cast<uint2 *>(QLh + at) = h2;
-                *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = l2;
+            if (qside) {  // q^ Gamma (stored when q is used)
+                split4_dot(ql, hi, lo);
+                *reinterpret_cast<uint2 *>(QLh + at) = hi;
+                *reinterpret_cast<uint2 *>(QLh + PL_CD + at) = lo;
             }
-            const uint32_t hw[4] = {hi.x, hi.x >> 16, hi.y, hi.y >> 16};
-            const uint32_t lw[4] = {lo.x, lo.x >> 16, lo.y, lo.y >> 16};
+            // the state update takes k^ / Gamma transposed: Kdiv^T[c][t] = k^_t[c] e^{-G_t[c]}
+            const uint32_t hw[4] = {h2.x, h2.x >> 16, h2.y, h2.y >> 16};
+            const uint32_t lw[4] = {l2.x, l2.x >> 16, l2.y, l2.y >> 16};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = ec0 + e;
@@ -657,6 +719,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             // 16w + ln; each row step waits for its own two operand loads (with more of them
             // in flight the loop needs registers that the matrix-core path then spills).
             // The lane offsets are rebuilt from an opaque thread index rather than kept live.
+            // First the previous chunk's epilogue, which reads the output rows this path rewrites.
+            epilogue_stage(ch);
+            __syncthreads();
             const int x = opaque(tid);
             const int lrow = 4 * ((x & 63) >> 4), lcol = ((x >> 6) << 4) + (x & 15);
             for (int u = 0; u < rend - r0; ++u) {
@@ -679,8 +744,6 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 const float r = row_group_sum((r4[0] + r4[1]) + (r4[2] + r4[3]));
-                // v_u is read by the four lanes of this column (one wave) before the lane
-                // with lh = 0 overwrites its slot with the output row below
                 const float du = BETA[u] * (VB[u * FPK + lcol] - r);
                 float o4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -698,10 +761,15 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 const float o = row_group_sum((o4[0] + o4[1]) + (o4[2] + o4[3]));
-                if (lrow == 0) VB[u * FPK + lcol] = o;
+                if (lrow == 0) OB[u * FPK + lcol] = o;
             }
+            next_loads(ch);
+            __syncthreads();
         } else {
             __builtin_amdgcn_s_setprio(2);
+            // the previous chunk's epilogue, on waves 4-7, which would otherwise wait in this phase
+            // for the triangular solve of wave 0
+            epilogue_stage(ch);
             // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
             if (wave == 0 || (wave == 1 && qside)) {
                 // the Gram blocks and T gate the next barrier for the whole workgroup: their
@@ -737,28 +805,35 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     // (A is strictly lower, so rows i <= k are left unchanged).  A goes through
                     // LDS k-major, AF[k][r][q] = A[4q + r][k], so that step k reads one float4.
                     {
-                        const float4 b4 = *reinterpret_cast<const float4 *>(BETA + 4 * lh);
+                        // LDS addresses here and below come from an opaque lane index: kept live
+                        // across the chunk loop they are spilled, and each reload waits for every
+                        // memory operation in flight, the next chunk's rows included
+                        const int lx = opaque(lane), lr = lx & 15, lg = lx >> 4;
+                        const float4 b4 = *reinterpret_cast<const float4 *>(BETA + 4 * lg);
                         const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) AF[ln * AFK + 4 * i + lh] = ln < 4 * lh + i ? acc[i] * bv[i] : 0.0f;
+                        for (int i = 0; i < 4; ++i) AF[lr * AFK + 4 * i + lg] = lr < 4 * lg + i ? acc[i] * bv[i] : 0.0f;
                     }
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                     __builtin_amdgcn_wave_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
                     const int x = opaque(lane), j = x >> 2, r = x & 3;
+                    // this lane's column of the A staging, one base address: step k's read is then
+                    // a constant offset from it
+                    const float *const afr = AF + opaque(4 * r);
                     // step k's A column is read TD steps ahead, so that the dependent chain of
                     // the substitution does not wait on LDS every other step
                     constexpr int TD = 6;
                     float4 af[C];
 #pragma unroll
-                    for (int k = 0; k < TD; ++k) af[k] = *reinterpret_cast<const float4 *>(AF + k * AFK + 4 * r);
+                    for (int k = 0; k < TD; ++k) af[k] = *reinterpret_cast<const float4 *>(afr + k * AFK);
                     float xv[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) xv[q] = (4 * q + r == j) ? 1.0f : 0.0f;
 #pragma unroll
                     for (int k = 0; k < C; ++k) {
                         __builtin_amdgcn_sched_barrier(0);
-                        if (k + TD < C) af[k + TD] = *reinterpret_cast<const float4 *>(AF + (k + TD) * AFK + 4 * r);
+                        if (k + TD < C) af[k + TD] = *reinterpret_cast<const float4 *>(afr + (k + TD) * AFK);
                         float xk;
                         switch (k & 3) {  // x_k, from lane 4j + k % 4 of the quad
                             case 0: xk = dpp<0x00>(xv[k >> 2]); break;
@@ -772,19 +847,21 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                         xv[2] = fmaf(-a.z, xk, xv[2]);
                         xv[3] = fmaf(-a.w, xk, xv[3]);
                     }
-                    const float bj = BETA[j];
+                    const int y = opaque(lane), yj = y >> 2, yr = y & 3;
+                    const float bj = BETA[yj];
+                    uint16_t *const tcol = TMh + yr * OPT + yj;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         uint16_t sh, sl;
                         split1(xv[q] * bj, sh, sl);
-                        TMh[(4 * q + r) * OPT + j] = sh;
-                        TMh[PL_CC + (4 * q + r) * OPT + j] = sl;
+                        tcol[4 * q * OPT] = sh;
+                        tcol[PL_CC + 4 * q * OPT] = sl;
                     }
                 } else {
-                    const int j = ln;
+                    const int y = opaque(lane), j = y & 15, lg = y >> 4;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * lh + i;
+                        const int r = 4 * lg + i;
                         uint16_t sh, sl;
                         split1(j <= r ? acc[i] : 0.0f, sh, sl);
                         PMh[r * OPT + j] = sh;
@@ -829,12 +906,23 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 const float x4[4] = {X[0], X[1], X[2], X[3]};
                 split4_dot(x4, Xs.h, Xs.l);
             }
-            // S has been read: decay it now, S <- Diag(Gamma_C) S, in the time the Gram / T
-            // waves need before the barrier (they decay theirs after it)
+            // Head gate: S has been read, so decay it now, S <- e^{G_C} S, in the time the Gram /
+            // T waves need before the barrier (they decay theirs after it).  Channel gates:
+            // the state update adds Kdiv^T U first and decays after it (phase 5).
             const bool late_decay = wave == 0;
+            // The next chunk's staging rewrites GH while slower waves may still be in the state
+            // update below (there is no barrier between them): the head gate takes the values it
+            // needs there now.
+            float4 gh_r = make_float4(0.f, 0.f, 0.f, 0.f);
+            float gh_last = 0.f, gh_exp = 0.f;
+            if (HEADG) {
+                gh_r = *reinterpret_cast<const float4 *>(GH + 4 * lh);
+                gh_last = GH[C - 1];
+                gh_exp = GH[C];
+            }
             auto decay = [&]() {
                 if (HEADG) {
-                    const float g = GH[C];  // e^{G_C}, one factor for the whole state
+                    const float g = gh_exp;  // e^{G_C}, one factor for the whole state
 #pragma unroll
                     for (int t = 0; t < 8; ++t) S[t] *= g;
                     return;
@@ -848,16 +936,20 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     S[t][3] *= g4.w;
                 }
             };
-            if (!late_decay) decay();
+            if (HEADG && !late_decay) decay();
             __syncthreads();
 
-            // ---- 5. U = T X, O = scale (Qbar S + P U), S <- Diag(Gamma_C) S + Khat^T U -------------
+            // ---- 5. U = T X, O = scale (Qbar S + P U), S <- Diag(Gamma_C) (S + Kdiv^T U) ----------
+            // (Khat = e^{G_C - G} (.) K = Diag(Gamma_C) Kdiv: the exit state Diag(Gamma_C) S +
+            // Khat^T U needs no plane of its own; Kdiv <= e^80 at the log-decay floor, and the
+            // vote bounds it by 2^116 without a floor, so the sum stays inside fp32)
             __builtin_amdgcn_s_setprio(3);  // the chunk's last dependent chain
             {
-                const uint2 Th = *reinterpret_cast<const uint2 *>(TMh + ln * OPT + 4 * lh);
-                const uint2 Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + ln * OPT + 4 * lh);
-                const uint2 Ph = *reinterpret_cast<const uint2 *>(PMh + ln * OPT + 4 * lh);
-                const uint2 Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + ln * OPT + 4 * lh);
+                const int y = opaque(lane), tp = (y & 15) * OPT + 4 * (y >> 4);
+                const uint2 Th = *reinterpret_cast<const uint2 *>(TMh + tp);
+                const uint2 Tl = *reinterpret_cast<const uint2 *>(TMh + PL_CC + tp);
+                const uint2 Ph = *reinterpret_cast<const uint2 *>(PMh + tp);
+                const uint2 Pl = *reinterpret_cast<const uint2 *>(PMh + PL_CC + tp);
                 const f32x4_t Uf = mma16x2(Th, Tl, Xs.h, Xs.l, f32x4_t{0.f, 0.f, 0.f, 0.f});
                 const Split4 Us(Uf);
                 if (qside) {
@@ -865,14 +957,14 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) OB[(4 * lh + i) * FPK + col] = O[i];
                 }
-                if (late_decay) decay();
-                // Khat^T U with the products split as in mma16x2.  Rows of odd tiles hold their
-                // two token pairs swapped (the plane's bank swizzle), so those tiles take the
-                // U operand with its pairs swapped to match.
+                if (HEADG && late_decay) decay();
+                // Kdiv^T U (head gate: K^T (Diag(e^{G_C - G}) U)) with the products split as in
+                // mma16x2.  Rows of odd tiles hold their two token pairs swapped (the plane's bank
+                // swizzle), so those tiles take the U operand with its pairs swapped to match.
                 Split4 Uk = Us;
                 if (HEADG) {  // Khat^T U = K^T (Diag(e^{G_C - G}) U): scale the rows of U
-                    const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
-                    const float gc = GH[C - 1];
+                    const float4 gr = gh_r;
+                    const float gc = gh_last;
                     const float u4[4] = {Uf[0] * __builtin_amdgcn_exp2f(gc - gr.x), Uf[1] * __builtin_amdgcn_exp2f(gc - gr.y),
                                          Uf[2] * __builtin_amdgcn_exp2f(gc - gr.z), Uf[3] * __builtin_amdgcn_exp2f(gc - gr.w)};
                     Uk = Split4(u4);
@@ -890,38 +982,21 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     S[t] = mma(a, (t & 1) ? ub_o : ub_e, S[t]);
                     S[t] = mma(a, (t & 1) ? ul_o : ul_e, S[t]);
                 }
+                if (!HEADG) decay();
             }
-            __builtin_amdgcn_s_setprio(0);  // the epilogue and the next staging
+            __builtin_amdgcn_s_setprio(0);  // the next staging
+            next_loads(ch);
         }
+        // No barrier between this chunk's state update and the next chunk's staging: the
+        // staging writes the K / Q / Kdiv planes (last read before the previous barrier), log
+        // alpha (read when the operands were built), beta (read by the triangular solve) and,
+        // for the head gate, GH (read into registers above); the state update reads T, P and
+        // Kdiv^T and writes the output rows, which nothing in the staging touches.
+    }
+    // the last chunk's epilogue, once its output rows are written
+    if (nchunks > 0) {
         __syncthreads();
-
-        // ---- 6. epilogue: sigma(g) * RMSNorm(o~) * w ------------------------------------------
-        if (!SEG || has_out) {
-            float o[4];
-            load4f((wide ? VB : OB) + et * FPK + ec0, o);
-            if (p.epilogue) {
-                float ss = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ss = fmaf(o[e], o[e], ss);
-                ss = half_wave_sum(ss);
-                const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.rms_eps);
-                float g[4], rw[4];
-                I4::unpack(graw, g);
-                load4f(RW + ec0, rw);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = sigmoidf_(g[e]) * (o[e] * inv) * rw[e];
-            }
-            OutStore4<OUT>::store(rows_view(o_base + static_cast<size_t>(r0) * HD * sizeof(OUT), rend - r0,
-                                            static_cast<uint32_t>(HD * sizeof(OUT)), D * sizeof(OUT)),
-                                  static_cast<uint32_t>(et) * static_cast<uint32_t>(HD * sizeof(OUT)) + ec0 * sizeof(OUT), o);
-        } else {
-            // runs without outputs still issue one (empty, dropped) store, so that every path
-            // leaves the same memory operations behind the next chunk's rows
-            __builtin_amdgcn_raw_buffer_store_b32(0u, rows_view(o_base, 0, 0, 0), 0u, 0, 0);
-        }
-        load_gate(ch + 1);
-        if (LOWRANK) load_z(ch + 1);
-        // the next chunk's first two barriers order these LDS reads before any rewrite
+        if (epi_wave && do_epi) epilogue(nchunks - 1);
     }
 
     // ---- final state and conv cache ------------------------------------------------------

@@ -10,9 +10,15 @@ Printed (one JSON line): prefill tokens/s as `value`, decode state GB/s
 (2 * B * H * 128^2 * 4 bytes per step / step time) beside it, a roofline
 entry for each kernel (algorithmic bytes per launch / mean launch time, from
 HIP events on the launch stream), and the fp64 CPU oracle timed on one
-sequence of the same workload on the host's cores.
+sequence of the same workload on the host's cores.  Also in the line: first,
+the measured ceilings of this GPU (a streaming HBM copy, an HBM read stream
+and a loop of bf16 matrix-core instructions), against which every fraction
+is also given beside the vendor's spec peaks; after the step loop, the
+long-context prefill (1 x 131072 tokens x 96 heads,
+random S0) and the packed variable-length prefill (64 lognormal lengths,
+578k tokens, per-sequence S0), each with its roofline fractions.
 
-    python bench.py [--steps K] [--warmup W] [--algo auto|chunked|recurrent]
+    python bench.py [--steps K] [--warmup W] [--algo auto|chunked|recurrent] [--no-long]
 """
 from __future__ import annotations
 
@@ -58,10 +64,66 @@ def decode_algorithmic_bytes(B: int, H: int) -> int:
     return state + act + conv
 
 
-def prefill_mfma_flops(T: int, H: int) -> int:
-    """Algorithmic MFMA flops of the chunked prefill at 64-token chunks with
-    16-token triangle granularity: 6 d^2 + 5 (C + 16) d per token-head."""
-    return T * H * (6 * D * D + 5 * (64 + 16) * D)
+def prefill_mfma_flops(T: int, H: int, C: int = 16) -> int:
+    """Matrix-core flops of the chunked algorithm at the kernel's chunk of C = 16 tokens,
+    per token-head (each contraction counted once, not the three bf16 products that
+    split operands take): X = V - Kbar S, Qbar S and the state update, 3 x 2 d^2; the
+    Gram blocks A and P, 2 x 2 C d; U = T X and P U, 2 x 2 C d.  = 114,688 at C = 16."""
+    return T * H * (6 * D * D + 8 * C * D)
+
+
+def measure_peaks(dev, stream, log, gib: int = 2) -> dict:
+    """This GPU's measured ceilings (libkda_peaks.so): a streaming copy of `gib` GiB (bytes
+    read + written / time), a read stream of the same size, and a loop of independent
+    v_mfma_f32_16x16x32_bf16 chains on every SIMD (dense bf16 flops / time).  Each is the
+    best of 5 timed launches after 2 warm-up launches."""
+    import ctypes
+    import torch
+    from gated_delta_rule_kda_amd import _build
+    L = ctypes.CDLL(_build.PEAKS_LIB)
+    for f in (L.kda_peak_copy, L.kda_peak_read, L.kda_peak_mfma):
+        f.restype = ctypes.c_int
+    L.kda_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    L.kda_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.kda_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    nbytes = gib << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    blocks = 256 * 32  # 8192 groups: the fastest copy of a sweep from 1024 to 32768
+    red = torch.empty(blocks, dtype=torch.int32, device=dev)
+    mblocks, iters = 256 * 8, 4096
+    mout = torch.empty(mblocks * 4, dtype=torch.float32, device=dev)
+    sp = stream.cuda_stream
+
+    def best(fn):
+        for _ in range(2):
+            assert fn() == 0
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            assert fn() == 0
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return min(ts)
+
+    t_copy = best(lambda: L.kda_peak_copy(src.data_ptr(), dst.data_ptr(), nbytes, blocks, sp))
+    t_read = best(lambda: L.kda_peak_read(src.data_ptr(), nbytes, red.data_ptr(), blocks, sp))
+    t_mfma = best(lambda: L.kda_peak_mfma(mout.data_ptr(), mblocks, iters, sp))
+    flops = mblocks * 4 * iters * 8 * 16 * 16 * 32 * 2
+    copy_gbps, read_gbps = 2 * nbytes / (t_copy * 1e-3) / 1e9, nbytes / (t_read * 1e-3) / 1e9
+    out = {"hbm_GBps": max(copy_gbps, read_gbps), "hbm_copy_GBps": copy_gbps, "hbm_read_GBps": read_gbps,
+           "mfma_bf16_TFLOPs": flops / (t_mfma * 1e-3) / 1e12,
+           "how": f"best of 5: {gib} GiB nontemporal 16-byte copy (bytes read + written) and read streams "
+                  f"over {blocks} 256-thread groups, hbm_GBps the faster; {mblocks * 4} waves x {iters} x 8 "
+                  f"independent 16x16x32 bf16 MFMAs"}
+    log(f"measured ceilings: copy {copy_gbps:.0f} GB/s, read {read_gbps:.0f} GB/s, "
+        f"bf16 MFMA {out['mfma_bf16_TFLOPs']:.0f} TFLOP/s")
+    del src, dst, red, mout
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_info() -> str:
@@ -134,68 +196,79 @@ def oracle_single_thread(W, oracle, decode_sample: int = 16) -> dict:
     return out
 
 
-def run_extra_workloads(kda, W, dev, stream, log, algo="auto") -> dict:
-    """Time the long-context (1 x 131072) and packed variable-length (64 sequences)
-    prefills, and the long context at 12 heads (one GPU's share of 96 heads split eight
-    ways): inputs generated one sequence at a time straight into device buffers.  The
-    long contexts are also timed in one sequential pass (the throughput variant) next to
-    AUTO's choice (the segmented prefill)."""
-    import dataclasses
+def time_long_workload(kda, W, dev, stream, log, name, spec, algos, reps=3, warmup=1) -> dict:
+    """Time one long prefill workload (all sequences start from a random S0): inputs are
+    generated one sequence at a time (the seeded generator the parity tests use) straight
+    into device buffers; each algorithm in `algos` is run `warmup` times, then timed over
+    `reps` launches with HIP events."""
     import torch
     out = {}
-    long12 = dataclasses.replace(W.workload("prefill_131072"), heads=12, name="prefill_131072_h12")
-    cases = [("prefill_131072", W.workload("prefill_131072"), [algo, "chunked_throughput"]),
-             ("prefill_131072_h12", long12, [algo, "chunked_throughput"]),
-             ("varlen_64", W.workload("varlen_64"), [algo])]
-    for name, spec, algos in cases:
-        lens = [int(x) for x in spec.lens]
-        N, H, T = len(lens), spec.heads, int(sum(lens))
-        bf = torch.bfloat16
-        bufs = {k: torch.empty((T, H, D), dtype=bf, device=dev) for k in ("q", "k", "v", "g")}
-        la = torch.empty((T, H, D), dtype=torch.float32, device=dev)
-        beta = torch.empty((T, H), dtype=torch.float32, device=dev)
-        s0 = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
-        t0 = time.perf_counter()
-        off = 0
-        cw = None
-        for n, L in enumerate(lens):
-            x = W.gen_prefill(W.PrefillSpec(lens=[L], heads=H, state_std=spec.state_std, seed=spec.seed,
-                                            first_seq=n))
-            for k in bufs:
-                bufs[k][off:off + L].copy_(torch.from_numpy(x[k]).to(bf))
-            la[off:off + L].copy_(torch.from_numpy(x["log_alpha"]))
-            beta[off:off + L].copy_(torch.from_numpy(x["beta"]))
-            s0[n].copy_(torch.from_numpy(x["state_in"][0]))
-            cw = x["conv_w"]
-            off += L
-        log(f"{name}: generated {T} tokens in {time.perf_counter() - t0:.1f}s")
-        cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
-        cwd = torch.from_numpy(cw).to(dev)
-        o = torch.empty((T, H, D), dtype=bf, device=dev)
-        s_out = torch.empty_like(s0)
-        for a in algos:
-            cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", prologue=True, epilogue=True, algo=a)
-            ws_n = kda.workspace_size(cfg, N, T)
-            ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    lens = [int(x) for x in spec.lens]
+    N, H, T = len(lens), spec.heads, int(sum(lens))
+    bf = torch.bfloat16
+    bufs = {k: torch.empty((T, H, D), dtype=bf, device=dev) for k in ("q", "k", "v", "g")}
+    la = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    beta = torch.empty((T, H), dtype=torch.float32, device=dev)
+    s0 = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    t0 = time.perf_counter()
+    off = 0
+    cw = None
+    for n, L in enumerate(lens):
+        x = W.gen_prefill(W.PrefillSpec(lens=[L], heads=H, state_std=spec.state_std, seed=spec.seed,
+                                        first_seq=n))
+        for k in bufs:
+            bufs[k][off:off + L].copy_(torch.from_numpy(x[k]).to(bf))
+        la[off:off + L].copy_(torch.from_numpy(x["log_alpha"]))
+        beta[off:off + L].copy_(torch.from_numpy(x["beta"]))
+        s0[n].copy_(torch.from_numpy(x["state_in"][0]))
+        cw = x["conv_w"]
+        off += L
+    log(f"{name}: generated {T} tokens in {time.perf_counter() - t0:.1f}s")
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=dev)
+    cwd = torch.from_numpy(cw).to(dev)
+    o = torch.empty((T, H, D), dtype=bf, device=dev)
+    s_out = torch.empty_like(s0)
+    for a in algos:
+        cfg = kda.config(H, io_dtype="bf16", out_dtype="bf16", prologue=True, epilogue=True, algo=a)
+        ws_n = kda.workspace_size(cfg, N, T)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
-            def run():
-                kda.prefill(bufs["q"], bufs["k"], bufs["v"], la, beta, cu, g=bufs["g"], conv_w=cwd,
-                            state_in=s0, o=o, state_out=s_out, workspace=ws if ws_n else None, cfg=cfg,
-                            stream=stream, return_conv=False)
+        def run():
+            kda.prefill(bufs["q"], bufs["k"], bufs["v"], la, beta, cu, g=bufs["g"], conv_w=cwd,
+                        state_in=s0, o=o, state_out=s_out, workspace=ws if ws_n else None, cfg=cfg,
+                        stream=stream, return_conv=False)
 
+        for _ in range(warmup):
             run()
-            torch.cuda.synchronize()
-            ms, med = time_events(run, 3, stream)
-            nb = prefill_algorithmic_bytes(T, H, N) + N * H * D * D * 4  # + the initial states read
-            key = name if a == algos[0] else f"{name}_{a}"
-            ran = kda.resolved_algo(cfg, N, T)
-            out[key] = {"tokens": T, "sequences": N, "heads": H, "max_len": max(lens), "algo": ran, "ms": ms,
-                        "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nb,
-                        "frac_of_hbm_roofline": nb / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}
-            log(f"{key} ({ran}): {ms:.2f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
-            del ws
-        del bufs, la, beta, s0, o, s_out
-        torch.cuda.empty_cache()
+        torch.cuda.synchronize()
+        ms, med = time_events(run, reps, stream)
+        nb = prefill_algorithmic_bytes(T, H, N) + N * H * D * D * 4  # + the initial states read
+        key = name if a == algos[0] else f"{name}_{a}"
+        ran = kda.resolved_algo(cfg, N, T)
+        out[key] = {"workload": f"{N} x {T // N if N == 1 else 'lognormal'} tokens, H={H}, d=128, full layer, "
+                                f"bf16 io, random fp32 S0", "tokens": T, "sequences": N, "heads": H,
+                    "max_len": max(lens), "algo": ran, "ms": ms, "ms_median": med, "reps": reps,
+                    "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nb,
+                    "GBps": nb / (ms * 1e-3) / 1e9,
+                    "frac_of_hbm_roofline": nb / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}
+        log(f"{key} ({ran}): {ms:.2f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
+        del ws
+    del bufs, la, beta, s0, o, s_out
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_extra_workloads(kda, W, dev, stream, log, algo="auto") -> dict:
+    """The long context in one sequential pass (the chunked kernel, next to AUTO's
+    segmented prefill in the main line) and at 12 heads (one GPU's share of 96 heads split
+    eight ways), by AUTO and in one pass."""
+    import dataclasses
+    out = {}
+    long12 = dataclasses.replace(W.workload("prefill_131072"), heads=12, name="prefill_131072_h12")
+    out.update(time_long_workload(kda, W, dev, stream, log, "prefill_131072_one_pass", W.workload("prefill_131072"),
+                                  ["chunked_throughput"]))
+    out.update(time_long_workload(kda, W, dev, stream, log, "prefill_131072_h12", long12,
+                                  [algo, "chunked_throughput"]))
     return out
 
 
@@ -376,7 +449,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--algo", default="auto",
-                    choices=["auto", "recurrent", "chunked", "chunked_throughput", "chunked_latency"])
+                    choices=["auto", "recurrent", "chunked", "chunked_throughput"])
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context and variable-length prefills and the measured ceilings "
+                         "(profiling runs of the main step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run one fp32 device copy of this many MiB after the timed region "
@@ -385,7 +461,8 @@ def main() -> int:
                     help="counter-derived HBM bytes per launch, used while the kernel sources "
                          "they were measured on are unchanged")
     ap.add_argument("--extra-workloads", action="store_true",
-                    help="also time the 131072-token and the 64-sequence variable-length prefills")
+                    help="also time the long context in one pass and at 12 heads, the gate variants "
+                         "and the serving cases")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the KDA core shards by head and by request with no "
@@ -454,6 +531,10 @@ def main() -> int:
         kda.decode_step(dq, dk_, dv_, dla, dbeta, dstate, g=dg, conv_w=dcw, conv_state=dconv,
                         o=do, cfg=dcfg, stream=stream)
 
+    # ---------------------------------------------------------------- this GPU's ceilings
+    # (first: they characterise the machine the rest runs on)
+    peaks = None if args.no_long else measure_peaks(dev, stream, log)
+
     # ---------------------------------------------------------------- timing
     for _ in range(args.warmup):
         run_prefill()
@@ -511,6 +592,16 @@ def main() -> int:
         log(f"oracle, one thread: {json.dumps(cpu1)}")
 
     traffic = load_traffic(args.traffic)
+    # the long-context and packed variable-length launches, and this GPU's measured ceilings
+    long_runs = None
+    if not args.no_long:
+        long_runs = {}
+        long_runs.update(time_long_workload(kda, W, dev, stream, log, "prefill_131072", W.workload("prefill_131072"),
+                                            [args.algo], reps=5, warmup=2))
+        long_runs.update(time_long_workload(kda, W, dev, stream, log, "varlen_64", W.workload("varlen_64"),
+                                            [args.algo], reps=5, warmup=2))
+        for e in long_runs.values():
+            e["frac_of_measured_hbm"] = e["GBps"] / peaks["hbm_GBps"]
     extra = None
     if args.extra_workloads:
         extra = run_extra_workloads(kda, W, dev, stream, log, args.algo)
@@ -538,7 +629,7 @@ def main() -> int:
                    "prefill_algo": algo_name, "global_batch": N, "seq_len": spec.lens[0],
                    "heads": H, "head_dim": D, "decode_batch": B},
         "prefill": {"ms": pre_mean, "ms_median": pre_med, "tokens_per_s": tok_s,
-                    "algorithmic_bytes": pb, "mfma_flops": pf,
+                    "algorithmic_bytes": pb, "mfma_flops_c16": pf,
                     "mfma_tflops": pf / (pre_mean * 1e-3) / 1e12,
                     "mfma_frac_of_peak": pf / (pre_mean * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                     "hbm_roofline_tokens_per_s": T / (pb / (HBM_PEAK_GBPS * 1e9))},
@@ -553,6 +644,14 @@ def main() -> int:
                             "traffic": traffic.get("decode")},
         "cpu_baseline": cpu,
     }
+    if peaks:
+        res["measured_ceilings"] = peaks
+        res["roofline"]["frac_of_measured"] = pre_gbps / peaks["hbm_GBps"]
+        res["roofline_decode"]["frac_of_measured"] = dec_gbps / peaks["hbm_GBps"]
+        res["prefill"]["mfma_frac_of_measured"] = pf / (pre_mean * 1e-3) / 1e12 / peaks["mfma_bf16_TFLOPs"]
+    if long_runs:
+        res["long_context"] = long_runs.get("prefill_131072")
+        res["varlen"] = long_runs.get("varlen_64")
     if cpu1:
         res["cpu_baseline_1thread"] = cpu1
     if copy_cal:

@@ -263,8 +263,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     const float l2_eps = p.l2_eps * (LOG2E * LOG2E);
     // low-rank gate: this lane's channel bias and e^{A_h} log2(e) (inside the sigmoid), or
     // e^{A_h} (outside the softplus, which works in log2 units)
-    const float gbias = LOWRANK ? p.gate_bias[hD + col] : 0.0f;
     const float gscale = LOWRANK ? __expf(p.gate_a[h]) * (SOFTPLUS ? 1.0f : LOG2E) : 0.0f;
+    // the bias times the factor that multiplies z + b (so that one fma forms it)
+    const float gbias = LOWRANK ? p.gate_bias[hD + col] * (SOFTPLUS ? LOG2E : gscale) : 0.0f;
 
     // ---- state slice in accumulator layout: S[t][i] = S(16t + 4lh + i, col) ----------------
     const int row_in = p.slots_in ? p.slots_in[n] : n;     // state_in / conv_in row
@@ -512,10 +513,14 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             // over the tokens: within the lane's 4 rows, then across the 4 row groups with
             // two lane permutes.  Rows past the end of the sequence get log alpha = 0, so
             // that they do not decay the carried state.
+            // (LDS addresses from an opaque lane index, as elsewhere: a spilled address costs a
+            // reload that waits for every memory operation in flight)
+            const int y = opaque(lane), yl = y & 15, yh = y >> 4, ycol = wave * 16 + yl;
             f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
+            const uint16_t *const zrow = ZL + yl * ZPK + 8 * yh;
 #pragma unroll
             for (int st = 0; st < 4; ++st)
-                if (st < zsteps) zacc = mma(*reinterpret_cast<const uint4 *>(ZL + ln * ZPK + 32 * st + 8 * lh), wb[st], zacc);
+                if (st < zsteps) zacc = mma(*reinterpret_cast<const uint4 *>(zrow + 32 * st), wb[st], zacc);
             float run[4];
             float acc_sum = 0.0f;
 #pragma unroll
@@ -524,27 +529,27 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 if (SOFTPLUS) {
                     // -e^{A_h} softplus(u) log2(e) = -e^{A_h} log2(1 + 2^t), t = u log2(e),
                     // as max(t, 0) + log2(1 + 2^-|t|) so that 2^t never overflows
-                    const float t = (zacc[i] + gbias) * LOG2E;
+                    const float t = fmaf(zacc[i], LOG2E, gbias);
                     la2 = -gscale * (fmaxf(t, 0.0f) + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-fabsf(t))));
                 } else {
-                    const float t = (zacc[i] + gbias) * gscale;  // e^{A_h} (z + b) log2(e)
+                    const float t = fmaf(zacc[i], gscale, gbias);  // e^{A_h} (z + b) log2(e)
                     la2 = (-5.0f * LOG2E) * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
                 }
-                la2 = r0 + 4 * lh + i < L ? la2 : 0.0f;
-                if (WIDE) AL[(4 * lh + i) * D + col] = __builtin_amdgcn_exp2f(la2);
+                la2 = r0 + 4 * yh + i < L ? la2 : 0.0f;
+                if (WIDE) AL[(4 * yh + i) * D + ycol] = __builtin_amdgcn_exp2f(la2);
                 acc_sum += la2;
                 run[i] = acc_sum;
             }
-            const int lid = lane;
-            float x1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lid - 16) * 4, __builtin_bit_cast(int, acc_sum)));
-            x1 = acc_sum + (lh >= 1 ? x1 : 0.0f);
-            float x2 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lid - 32) * 4, __builtin_bit_cast(int, x1)));
-            x2 = x1 + (lh >= 2 ? x2 : 0.0f);
+            float x1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((y - 16) * 4, __builtin_bit_cast(int, acc_sum)));
+            x1 = acc_sum + (yh >= 1 ? x1 : 0.0f);
+            float x2 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((y - 32) * 4, __builtin_bit_cast(int, x1)));
+            x2 = x1 + (yh >= 2 ? x2 : 0.0f);
             const float before = x2 - acc_sum;  // sum over the rows of the earlier row groups
+            float *const larow = LA + 4 * yh * D + ycol;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) LA[(4 * lh + i) * D + col] = run[i] + before;
-            if (lh == 3) {
-                EGC[col] = __builtin_amdgcn_exp2f(run[3] + before);
+            for (int i = 0; i < 4; ++i) larow[i * D] = run[i] + before;
+            if (yh == 3) {
+                EGC[ycol] = __builtin_amdgcn_exp2f(run[3] + before);
                 if (WIDE && run[3] + before < -WIDE_LOG2) *FLAG = 1;
             }
         }
@@ -971,13 +976,16 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 }
                 const uint4 ub_e = make_uint4(Uk.h.x, Uk.h.y, Uk.h.x, Uk.h.y), ul_e = make_uint4(Uk.l.x, Uk.l.y, 0u, 0u);
                 const uint4 ub_o = make_uint4(Uk.h.y, Uk.h.x, Uk.h.y, Uk.h.x), ul_o = make_uint4(Uk.l.y, Uk.l.x, 0u, 0u);
+                // (an opaque lane index for the gates whose register pressure otherwise spills
+                // these addresses; the compiler keeps them in registers for the others)
+                const int yk = (LOWRANK || WIDE) ? opaque(lane) : lane, ykl = yk & 15, ykh = yk >> 4;
+                const uint16_t *const krow = KHTh + ykl * KHTR;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
-                    const int c = 16 * t + ln;
-                    // tokens 4lh .. 4lh+3 of row c sit at group lh ^ (t / 2)
-                    const int ka = c * KHTR + 4 * (lh ^ (t >> 1));
-                    const uint2 ah = *reinterpret_cast<const uint2 *>(KHTh + ka);
-                    const uint2 al = *reinterpret_cast<const uint2 *>(KHTh + C + ka);
+                    // tokens 4lh .. 4lh+3 of row c = 16 t + ln sit at group lh ^ (t / 2)
+                    const int ka = 16 * t * KHTR + 4 * (ykh ^ (t >> 1));
+                    const uint2 ah = *reinterpret_cast<const uint2 *>(krow + ka);
+                    const uint2 al = *reinterpret_cast<const uint2 *>(krow + C + ka);
                     const uint4 a = make_uint4(ah.x, ah.y, al.x, al.y);
                     S[t] = mma(a, (t & 1) ? ub_o : ub_e, S[t]);
                     S[t] = mma(a, (t & 1) ? ul_o : ul_e, S[t]);

@@ -102,6 +102,15 @@ __device__ __forceinline__ void split4_dot(const float *x, uint2 &hi, uint2 &lo)
     lo = make_uint2(pack_bf16(r0, r1), pack_bf16(r2, r3));
 }
 
+// The four bf16 values of a pair of packed words written to p[0], p[stride], p[2 stride]
+// and p[3 stride] (a column or row of a 16-bit plane).
+__device__ __forceinline__ void store_halves(uint16_t *p, int stride, uint2 w) {
+    p[0] = static_cast<uint16_t>(w.x);
+    p[stride] = static_cast<uint16_t>(w.x >> 16);
+    p[2 * stride] = static_cast<uint16_t>(w.y);
+    p[3 * stride] = static_cast<uint16_t>(w.y >> 16);
+}
+
 // Two groups of four floats split with one block of dot products.
 __device__ __forceinline__ void split4x2_dot(const float *x, const float *y, uint2 &xh, uint2 &xl, uint2 &yh, uint2 &yl) {
     const float v[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
@@ -148,10 +157,10 @@ __device__ __forceinline__ f32x4_t mma16_3(uint2 ahi, uint2 alo, uint2 bhi, uint
 struct Split4 {
     uint2 h, l;
     Split4() = default;
-    __device__ __forceinline__ explicit Split4(const float *x) { split4(x, h, l); }
+    __device__ __forceinline__ explicit Split4(const float *x) { split4_dot(x, h, l); }
     __device__ __forceinline__ explicit Split4(const f32x4_t &x) {
         const float v[4] = {x[0], x[1], x[2], x[3]};
-        split4(v, h, l);
+        split4_dot(v, h, l);
     }
 };
 

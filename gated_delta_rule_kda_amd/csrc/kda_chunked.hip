@@ -855,23 +855,20 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     const int y = opaque(lane), yj = y >> 2, yr = y & 3;
                     const float bj = BETA[yj];
                     uint16_t *const tcol = TMh + yr * OPT + yj;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        uint16_t sh, sl;
-                        split1(xv[q] * bj, sh, sl);
-                        tcol[4 * q * OPT] = sh;
-                        tcol[PL_CC + 4 * q * OPT] = sl;
-                    }
+                    const float tv[4] = {xv[0] * bj, xv[1] * bj, xv[2] * bj, xv[3] * bj};
+                    uint2 th, tl;
+                    split4_dot(tv, th, tl);
+                    store_halves(tcol, 4 * OPT, th);
+                    store_halves(tcol + PL_CC, 4 * OPT, tl);
                 } else {
                     const int y = opaque(lane), j = y & 15, lg = y >> 4;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * lg + i;
-                        uint16_t sh, sl;
-                        split1(j <= r ? acc[i] : 0.0f, sh, sl);
-                        PMh[r * OPT + j] = sh;
-                        PMh[PL_CC + r * OPT + j] = sl;
-                    }
+                    const int r = 4 * lg;
+                    const float pv[4] = {j <= r ? acc[0] : 0.0f, j <= r + 1 ? acc[1] : 0.0f,
+                                         j <= r + 2 ? acc[2] : 0.0f, j <= r + 3 ? acc[3] : 0.0f};
+                    uint2 ph, pl;
+                    split4_dot(pv, ph, pl);
+                    store_halves(PMh + r * OPT + j, OPT, ph);
+                    store_halves(PMh + PL_CC + r * OPT + j, OPT, pl);
                 }
                 __builtin_amdgcn_s_setprio(2);
             }

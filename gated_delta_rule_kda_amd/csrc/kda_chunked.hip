@@ -366,20 +366,26 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             wb[st] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     };
-    // The epilogue of a chunk runs on waves 4-7 during the next chunk's Gram / T phase, where
-    // they would otherwise wait for the triangular solve of wave 0: thread x = tid - 256 takes
-    // token x / 16 and channels 8 (x % 16) .. + 7, so a token's 128 channels form one 16-lane
-    // row and its RMS sum takes four DPP steps.  Every wave issues the same memory operations
-    // in the same order whether or not it has outputs (views without bytes are dropped without
-    // a memory access), so that the wait for a chunk's rows always counts the same younger
-    // operations and never has to wait for an output store as well.
-    constexpr int EPI_WAVE = 4;
-    const bool epi_wave = wave >= EPI_WAVE;
+    // The epilogue of a chunk runs on waves 2, 3, 6 and 7 during the next chunk's Gram / T
+    // phase, where they would otherwise wait for the triangular solve of wave 0.  Wave w shares
+    // its SIMD with wave w + 4, so these four waves sit on the two SIMDs that do not host the
+    // Gram / T waves 0 and 1 (on waves 4-7 instead, the epilogue took issue slots from them and
+    // the launch ran 2.5% longer).  Epilogue thread x (0 .. 255, waves 2, 3, 6, 7 in order)
+    // takes token x / 16 and channels 8 (x % 16) .. + 7, so a token's 128 channels form one
+    // 16-lane row and its RMS sum takes four DPP steps.  Every wave issues the same memory
+    // operations in the same order whether or not it has outputs (views without bytes are
+    // dropped without a memory access), so that the wait for a chunk's rows always counts the
+    // same younger operations and never has to wait for an output store as well.
+    const bool epi_wave = (wave & 2) != 0;
+    auto epi_thread = [&]() {
+        const int t = opaque(tid), w = t >> 6;
+        return ((((w >> 1) & 2) | (w & 1)) << 6) | (t & 63);
+    };
     const bool do_epi = !SEG || has_out;
     typename Vec8<IO>::Raw graw;
     // g rows of chunk c for the epilogue threads (use = false: an empty load in their place)
     auto load_gate = [&](int c, bool use) {
-        const int x = opaque(tid) - EPI_WAVE * 64;
+        const int x = epi_thread();
         use = use && p.epilogue && do_epi && epi_wave;
         const int r0 = c * C;
         const int nrow = use ? min(L, r0 + C) - r0 : 0;
@@ -393,9 +399,9 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0u, 0, 0);
         if (sizeof(OUT) == 4) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0u, 0, 0);
     };
-    // sigma(g) * RMSNorm(o~) * w of chunk c from its output rows (waves 4-7 only)
+    // sigma(g) * RMSNorm(o~) * w of chunk c from its output rows (epilogue waves only)
     auto epilogue = [&](int c) {
-        const int x = opaque(tid) - EPI_WAVE * 64, xt = x >> 4, xc = (x & 15) * 8;
+        const int x = epi_thread(), xt = x >> 4, xc = (x & 15) * 8;
         const int r0 = c * C, nrow = min(L, r0 + C) - r0;
         float o[8];
         load4f(OB + xt * FPK + xc, o);
@@ -772,8 +778,8 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             __syncthreads();
         } else {
             __builtin_amdgcn_s_setprio(2);
-            // the previous chunk's epilogue, on waves 4-7, which would otherwise wait in this phase
-            // for the triangular solve of wave 0
+            // the previous chunk's epilogue, on waves 2, 3, 6, 7, which would otherwise wait in this
+            // phase for the triangular solve of wave 0
             epilogue_stage(ch);
             // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
             if (wave == 0 || (wave == 1 && qside)) {

@@ -87,9 +87,7 @@ constexpr int OFF_LA = OFF_V + C * FPK * 4;          // log2(alpha) -> cumulativ
 // fp32 [16][132] output rows of a chunk: written at its state update, read by its epilogue
 // during the next chunk's Gram / T phase
 constexpr int OFF_O = OFF_LA + C * D * 4;
-constexpr int AFK = 16;                              // row of the A staging (k-major)
-constexpr int OFF_AF = OFF_O + C * FPK * 4;          // A (beta-scaled) fp32 [16][4][4], rows of AFK
-constexpr int OFF_PM = OFF_AF + C * AFK * 4;         // P                                        hi,lo [16][20]
+constexpr int OFF_PM = OFF_O + C * FPK * 4;          // P                                        hi,lo [16][20]
 constexpr int OFF_TM = OFF_PM + 2 * PL_CC * 2;       // T                                        hi,lo [16][20]
 constexpr int OFF_BETA = OFF_TM + 2 * PL_CC * 2;     // fp32 [16]
 constexpr int OFF_EGC = OFF_BETA + C * 4;            // e^{G_C} fp32 [128]
@@ -205,7 +203,6 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     float *const OB = reinterpret_cast<float *>(smem + OFF_O);
     float *const VB = reinterpret_cast<float *>(smem + OFF_V);
     float *const LA = reinterpret_cast<float *>(smem + OFF_LA);
-    float *const AF = reinterpret_cast<float *>(smem + OFF_AF);
     float *const BETA = reinterpret_cast<float *>(smem + OFF_BETA);
     float *const EGC = reinterpret_cast<float *>(smem + OFF_EGC);
     float *const CW = reinterpret_cast<float *>(smem + OFF_CW);
@@ -786,86 +783,76 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                 // the Gram blocks and T gate the next barrier for the whole workgroup: their
                 // waves take issue priority over the other waves of their SIMDs meanwhile
                 __builtin_amdgcn_s_setprio(3);
-                const uint16_t *Lh = wave == 0 ? KLh : QLh;
+                const bool tw = wave == 0;
+                // Wave 0 forms its tile transposed, Kdiv Kbar^T, so that lane (lh, ln) holds row
+                // ln of A (columns 4lh .. 4lh+3); wave 1 forms P = Qbar Kdiv^T as it stands.  The
+                // beta values the solve needs are read before the products, off its chain.
+                float bs = 0.f;
+                float4 bc = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (tw) {
+                    const int x = opaque(lane);
+                    bs = BETA[x & 15];
+                    bc = *reinterpret_cast<const float4 *>(BETA + 4 * (x >> 4));
+                }
+                const uint16_t *const Ap = tw ? (HEADG ? KLh : KRDh) : QLh;
+                const uint16_t *const Bp = tw ? KLh : (HEADG ? KLh : KRDh);  // k^ / Gamma, or k^ for the head gate
                 // two independent accumulation chains (channels 0-63 and 64-127) halve the
                 // dependent-MFMA latency on this critical path
                 f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
                 for (int s = 0; s < D / 32; ++s) {
                     const int ka = ln * OPK + 32 * s + 8 * lh;
-                    const uint4 ah = *reinterpret_cast<const uint4 *>(Lh + ka);
-                    const uint4 al = *reinterpret_cast<const uint4 *>(Lh + PL_CD + ka);
-                    const uint16_t *Bp = HEADG ? KLh : KRDh;  // k^ / Gamma, or k^ for the head gate
+                    const uint4 ah = *reinterpret_cast<const uint4 *>(Ap + ka);
+                    const uint4 al = *reinterpret_cast<const uint4 *>(Ap + PL_CD + ka);
                     const uint4 bh = *reinterpret_cast<const uint4 *>(Bp + ka);
                     const uint4 bl = *reinterpret_cast<const uint4 *>(Bp + PL_CD + ka);
                     acc2[s >> 1] = mma3(ah, al, bh, bl, acc2[s >> 1]);
                 }
                 f32x4_t acc = acc2[0] + acc2[1];
-                if (HEADG) {  // row s, column j of the Gram tile times e^{G_s - G_j} (<= 1 for j <= s)
-                    const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);
-                    const float gj = GH[ln];
-                    acc[0] *= __builtin_amdgcn_exp2f(fminf(gr.x - gj, 0.0f));
-                    acc[1] *= __builtin_amdgcn_exp2f(fminf(gr.y - gj, 0.0f));
-                    acc[2] *= __builtin_amdgcn_exp2f(fminf(gr.z - gj, 0.0f));
-                    acc[3] *= __builtin_amdgcn_exp2f(fminf(gr.w - gj, 0.0f));
+                if (HEADG) {  // entry (s, j) of the Gram tile times e^{G_s - G_j} (<= 1 for j <= s)
+                    const float4 g4 = *reinterpret_cast<const float4 *>(GH + 4 * lh);
+                    const float g1 = GH[ln];
+                    const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)  // wave 0's tile is transposed: s = ln, j = 4lh + i
+                        acc[i] *= __builtin_amdgcn_exp2f(fminf(tw ? g1 - gv[i] : gv[i] - g1, 0.0f));
                 }
-                if (wave == 0) {
-                    // T = (I + A)^{-1} Diag(beta) by forward substitution in fp32: lane 4j + r
-                    // carries rows r, r+4, r+8, r+12 of column j of (I + A)^{-1}; step k
-                    // broadcasts row k inside the quad and removes A[i][k] x_k from every row
-                    // (A is strictly lower, so rows i <= k are left unchanged).  A goes through
-                    // LDS k-major, AF[k][r][q] = A[4q + r][k], so that step k reads one float4.
-                    {
-                        // LDS addresses here and below come from an opaque lane index: kept live
-                        // across the chunk loop they are spilled, and each reload waits for every
-                        // memory operation in flight, the next chunk's rows included
-                        const int lx = opaque(lane), lr = lx & 15, lg = lx >> 4;
-                        const float4 b4 = *reinterpret_cast<const float4 *>(BETA + 4 * lg);
-                        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+                if (tw) {
+                    // T = (I + A)^{-1} Diag(beta) by forward substitution in fp32.  Lane (c, r) =
+                    // 16c + r carries row r of X = (I + A)^{-1}, columns 4c .. 4c+3, and the whole
+                    // of row r of -A in registers: the lane's own four entries, A[r][4lh + i] =
+                    // beta_r Gram[r][4lh + i] for 4lh + i < r, gathered from the four 16-lane rows
+                    // of the wave with the gfx950 row swaps.  Step k then adds -A[r][k] X[k][j],
+                    // X[k][j] broadcast from lane k of the lane's own 16-lane row (DPP
+                    // row_newbcast), as one multiply-add per column: no LDS on the chain, and
+                    // each step depends on the previous one through one instruction.
+                    const int x = opaque(lane), r = x & 15, c = x >> 4;
+                    float na[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) AF[lr * AFK + 4 * i + lg] = lr < 4 * lg + i ? acc[i] * bv[i] : 0.0f;
+                    for (int i = 0; i < 4; ++i) na[i] = 4 * c + i < r ? -(acc[i] * bs) : 0.0f;
+                    float nA[C];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // permlane16_swap: rows 0, 1 get row 0 (first result) and row 1 (second),
+                        // rows 2, 3 get rows 2 and 3; permlane32_swap then spreads each to all rows
+                        const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(na[i]), __float_as_uint(na[i]), false, false);
+                        const auto q = __builtin_amdgcn_permlane32_swap(pr[0], pr[0], false, false);
+                        const auto w = __builtin_amdgcn_permlane32_swap(pr[1], pr[1], false, false);
+                        nA[i] = __uint_as_float(q[0]);       // row group 0: columns 0 .. 3
+                        nA[4 + i] = __uint_as_float(w[0]);   // row group 1
+                        nA[8 + i] = __uint_as_float(q[1]);   // row group 2
+                        nA[12 + i] = __uint_as_float(w[1]);  // row group 3
                     }
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                    __builtin_amdgcn_wave_barrier();
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-                    const int x = opaque(lane), j = x >> 2, r = x & 3;
-                    // this lane's column of the A staging, one base address: step k's read is then
-                    // a constant offset from it
-                    const float *const afr = AF + opaque(4 * r);
-                    // step k's A column is read TD steps ahead, so that the dependent chain of
-                    // the substitution does not wait on LDS every other step
-                    constexpr int TD = 6;
-                    float4 af[C];
-#pragma unroll
-                    for (int k = 0; k < TD; ++k) af[k] = *reinterpret_cast<const float4 *>(afr + k * AFK);
                     float xv[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) xv[q] = (4 * q + r == j) ? 1.0f : 0.0f;
-#pragma unroll
-                    for (int k = 0; k < C; ++k) {
-                        __builtin_amdgcn_sched_barrier(0);
-                        if (k + TD < C) af[k + TD] = *reinterpret_cast<const float4 *>(afr + (k + TD) * AFK);
-                        float xk;
-                        switch (k & 3) {  // x_k, from lane 4j + k % 4 of the quad
-                            case 0: xk = dpp<0x00>(xv[k >> 2]); break;
-                            case 1: xk = dpp<0x55>(xv[k >> 2]); break;
-                            case 2: xk = dpp<0xAA>(xv[k >> 2]); break;
-                            default: xk = dpp<0xFF>(xv[k >> 2]); break;
-                        }
-                        const float4 a = af[k];
-                        xv[0] = fmaf(-a.x, xk, xv[0]);
-                        xv[1] = fmaf(-a.y, xk, xv[1]);
-                        xv[2] = fmaf(-a.z, xk, xv[2]);
-                        xv[3] = fmaf(-a.w, xk, xv[3]);
-                    }
-                    const int y = opaque(lane), yj = y >> 2, yr = y & 3;
-                    const float bj = BETA[yj];
-                    uint16_t *const tcol = TMh + yr * OPT + yj;
-                    const float tv[4] = {xv[0] * bj, xv[1] * bj, xv[2] * bj, xv[3] * bj};
+                    for (int m = 0; m < 4; ++m) xv[m] = r == 4 * c + m ? 1.0f : 0.0f;
+                    forward_substitute16(xv, nA);
+                    const float tv[4] = {xv[0] * bc.x, xv[1] * bc.y, xv[2] * bc.z, xv[3] * bc.w};
                     uint2 th, tl;
                     split4_dot(tv, th, tl);
-                    store_halves(tcol, 4 * OPT, th);
-                    store_halves(tcol + PL_CC, 4 * OPT, tl);
+                    // row r, columns 4c .. 4c+3: the A operand the state update reads in this lane
+                    *reinterpret_cast<uint2 *>(TMh + r * OPT + 4 * c) = th;
+                    *reinterpret_cast<uint2 *>(TMh + PL_CC + r * OPT + 4 * c) = tl;
                 } else {
                     const int y = opaque(lane), j = y & 15, lg = y >> 4;
                     const int r = 4 * lg;

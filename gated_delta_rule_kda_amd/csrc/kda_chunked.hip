@@ -308,7 +308,8 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                           : HEADG ? reinterpret_cast<const char *>(p.log_alpha + static_cast<size_t>(t0) * H + h)
                                   : reinterpret_cast<const char *>(p.log_alpha + first);
     const char *beta_base = reinterpret_cast<const char *>(p.beta + static_cast<size_t>(t0) * H + h);
-    const char *g_base = p.epilogue ? static_cast<const char *>(p.g) + first * sizeof(IO) : nullptr;
+    // (without an epilogue the g views hold no rows and read nothing: any base will do)
+    const char *g_base = static_cast<const char *>(p.epilogue ? p.g : p.q) + first * sizeof(IO);
     char *o_base = static_cast<char *>(p.o) + first * sizeof(OUT);
 
     // Per-thread offsets of the prefetches are rebuilt from an opaque copy of the thread
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         use = use && p.epilogue && do_epi && epi_wave;
         const int r0 = c * C;
         const int nrow = use ? min(L, r0 + C) - r0 : 0;
-        const char *const gb = use ? g_base + static_cast<size_t>(r0) * rowb_io : static_cast<const char *>(p.q);
+        const char *const gb = g_base + static_cast<size_t>(r0) * rowb_io;  // no rows when unused
         graw = BufLoad8<IO>::load(rows_view(gb, nrow, rowb_io, D * sizeof(IO)),
                                   use ? static_cast<uint32_t>(x >> 4) * rowb_io + (x & 15) * 8 * sizeof(IO) : 0u);
     };

@@ -306,9 +306,8 @@ def run_lowrank_gate_workload(kda, W, dev, stream, log, rank=128, softplus=False
                     conv_out=c_out, gate_z=gz, gate_w=gw, gate_bias=gb, gate_a=ga, workspace=ws, cfg=cfg,
                     stream=stream)
 
-    run()
-    torch.cuda.synchronize()
-    ms, _ = time_events(run, 10, stream)
+    warm_up(run)
+    ms, _ = time_events(run, 20, stream)
     nb = prefill_algorithmic_bytes(T, H, N, gate_rank=rank)
     name = "prefill_4x4096_" + (f"softplus_gate_wild{wild_every}" if softplus else "lowrank_gate")
     log(f"{name} (r={rank}): {ms:.3f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
@@ -340,9 +339,8 @@ def run_head_gate_workload(kda, W, dev, stream, log) -> dict:
         kda.prefill(t["q"], t["k"], t["v"], la, beta, cu, g=t["g"], conv_w=cw, o=o, state_out=s_out,
                     conv_out=c_out, workspace=ws, cfg=cfg, stream=stream)
 
-    run()
-    torch.cuda.synchronize()
-    ms, _ = time_events(run, 10, stream)
+    warm_up(run)
+    ms, _ = time_events(run, 20, stream)
     nb = prefill_algorithmic_bytes(T, H, N, head_gate=True)
     log(f"prefill_4x4096 per-head gate: {ms:.3f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
     return {"prefill_4x4096_head_gate": {"tokens": T, "ms": ms, "tokens_per_s": T / (ms * 1e-3),
@@ -385,8 +383,8 @@ def run_serving_workloads(kda, dev, stream, log, H=96, B=256, drafts=4) -> dict:
         kda.decode_step(q, k, v, la, beta, pool, g=g, conv_w=cw, conv_state=conv, slots=s_in,
                         slots_out=s_out, o=o, cfg=cfg, stream=stream)
 
-    cow()
-    ms, _ = time_events(cow, 10, stream)
+    warm_up(cow)
+    ms, _ = time_events(cow, 20, stream)
     out["decode_copy_on_write"] = {"requests": B, "heads": H, "ms": ms,
                                    "state_GBps": 2 * B * H * D * D * 4 / (ms * 1e-3) / 1e9}
     log(f"decode copy-on-write: {ms:.4f} ms, {out['decode_copy_on_write']['state_GBps']:.0f} GB/s of state")
@@ -417,9 +415,10 @@ def run_serving_workloads(kda, dev, stream, log, H=96, B=256, drafts=4) -> dict:
                     state_in=pool, state_out=pool, o=o_acc, state_in_slots=slots, state_out_slots=slots,
                     workspace=ws, cfg=cfg, stream=stream)
 
-    verify()
-    vms, _ = time_events(verify, 10, stream)
-    rms_, _ = time_events(replay, 10, stream)
+    warm_up(verify)
+    vms, _ = time_events(verify, 20, stream)
+    warm_up(replay, 5)
+    rms_, _ = time_events(replay, 20, stream)
     out["speculative_round"] = {"requests": B, "heads": H, "draft_tokens": drafts, "accepted_tokens": Ta,
                                 "verify_ms": vms, "replay_ms": rms_,
                                 "verified_tokens_per_s": T / (vms * 1e-3)}
@@ -427,6 +426,15 @@ def run_serving_workloads(kda, dev, stream, log, H=96, B=256, drafts=4) -> dict:
     del pool, conv
     torch.cuda.empty_cache()
     return out
+
+
+def warm_up(fn, n: int = 20):
+    """n untimed calls, then a device synchronisation: the clocks of a fresh box settle over
+    the first launches (up to 20% slower than later ones)."""
+    import torch
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
 
 
 def time_events(fn, steps: int, stream):

@@ -59,7 +59,8 @@ def to_np(t) -> Optional[np.ndarray]:
 def gpu_prefill(inp: Dict[str, np.ndarray], io: str = "bf16", out: str = "f32", algo: str = "auto",
                 prologue: Optional[bool] = None, epilogue: Optional[bool] = None,
                 rms_w: Optional[np.ndarray] = None, in_place: bool = False,
-                keep_device: bool = False, gate: str = "log_alpha", beta_mode: str = "value"):
+                keep_device: bool = False, gate: str = "log_alpha", beta_mode: str = "value",
+                stream=None, churn: bool = False):
     import torch
     import gated_delta_rule_kda_amd as kda
     io_t = torch.bfloat16 if io == "bf16" else torch.float32
@@ -79,9 +80,16 @@ def gpu_prefill(inp: Dict[str, np.ndarray], io: str = "bf16", out: str = "f32", 
         kw["state_out"] = s0
     if in_place and d["conv_in"] is not None:
         kw["conv_out"] = d["conv_in"]
+    if stream is not None:
+        kw["stream"] = stream
     o, s, c = kda.prefill(d["q"], d["k"], d["v"], la, b, cu, g=d["g"] if epilogue else None,
                           conv_w=cw, conv_in=d["conv_in"] if prologue else None, rms_w=rw,
                           state_in=s0, cfg=cfg, **kw)
+    if churn:
+        # allocations and writes on the current stream while the call may still run on
+        # `stream`: memory the call freed early would be handed out and overwritten here
+        for _ in range(8):
+            torch.full((1 << 20,), -7.0, device=o.device).add_(1.0)
     torch.cuda.synchronize()
     if keep_device:
         return o, s, c

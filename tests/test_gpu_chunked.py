@@ -194,6 +194,25 @@ def test_varlen_subset(algo):
     _check(g, r, "bf16")
 
 
+def test_side_stream_owns_its_allocations():
+    """prefill on a side stream with no workspace or outputs passed: the binding allocates
+    them for that stream (the longest-first order table and, for the segmented prefill, its
+    M / B matrices), so allocations queued on the current stream right after cannot take
+    that memory while the kernels still run.  The results equal the same calls on the
+    current stream bit for bit, and the oracle."""
+    import torch
+    inp = W.gen_prefill(W.PrefillSpec(lens=[300, 17, 129, 64], heads=3, state_std=0.02, conv_in=True, seed=71))
+    r = oracle_prefill(inp)
+    side = torch.cuda.Stream()
+    for algo in ("chunked_throughput", "chunked_scan"):
+        say(f"side stream: {algo}")
+        ref = gpu_prefill(inp, io="bf16", out="f32", algo=algo)
+        g = gpu_prefill(inp, io="bf16", out="f32", algo=algo, stream=side, churn=True)
+        for n in ("o", "state", "conv"):
+            assert np.array_equal(g[n], ref[n]), (algo, n)
+        _check(g, r, "f32")
+
+
 def test_full_size_prefill_sampled():
     """The benchmark's launch (4 x 4096 tokens, 96 heads, bf16 io and output, AUTO
     algorithm): all 96 heads of sequence 0 and one head of each other sequence against the

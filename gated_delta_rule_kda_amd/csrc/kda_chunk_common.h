@@ -278,6 +278,42 @@ __device__ __forceinline__ void forward_substitute16(float *x, const float *nA) 
           "v"(nA[8]), "v"(nA[9]), "v"(nA[10]), "v"(nA[11]), "v"(nA[12]), "v"(nA[13]), "v"(nA[14]), "v"(nA[15]));
 }
 
+// Steps k0 .. k0+3 of the same substitution (four calls, k0 = 0, 4, 8, 12, make the whole), so
+// that independent work can be placed between them; each part starts with the two wait
+// states its first DPP read needs after whatever vector instruction wrote x last.
+#define KDA_FS4_BODY(K0, K1, K2, K3)                                                          \
+    asm volatile(                                                                             \
+        "s_nop 1\n\t"                                                                         \
+        "v_fmac_f32_dpp %0, %0, %4 row_newbcast:" #K0 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %1, %1, %4 row_newbcast:" #K0 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %2, %2, %4 row_newbcast:" #K0 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %3, %3, %4 row_newbcast:" #K0 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %0, %0, %5 row_newbcast:" #K1 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %1, %1, %5 row_newbcast:" #K1 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %2, %2, %5 row_newbcast:" #K1 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %3, %3, %5 row_newbcast:" #K1 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %0, %0, %6 row_newbcast:" #K2 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %1, %1, %6 row_newbcast:" #K2 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %2, %2, %6 row_newbcast:" #K2 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %3, %3, %6 row_newbcast:" #K2 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %0, %0, %7 row_newbcast:" #K3 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %1, %1, %7 row_newbcast:" #K3 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %2, %2, %7 row_newbcast:" #K3 " row_mask:0xf bank_mask:0xf\n\t"       \
+        "v_fmac_f32_dpp %3, %3, %7 row_newbcast:" #K3 " row_mask:0xf bank_mask:0xf\n\t"       \
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])                                      \
+        : "v"(nA[K0]), "v"(nA[K1]), "v"(nA[K2]), "v"(nA[K3]))
+template <int K0>
+__device__ __forceinline__ void forward_substitute4(float *x, const float *nA);
+template <>
+__device__ __forceinline__ void forward_substitute4<0>(float *x, const float *nA) { KDA_FS4_BODY(0, 1, 2, 3); }
+template <>
+__device__ __forceinline__ void forward_substitute4<4>(float *x, const float *nA) { KDA_FS4_BODY(4, 5, 6, 7); }
+template <>
+__device__ __forceinline__ void forward_substitute4<8>(float *x, const float *nA) { KDA_FS4_BODY(8, 9, 10, 11); }
+template <>
+__device__ __forceinline__ void forward_substitute4<12>(float *x, const float *nA) { KDA_FS4_BODY(12, 13, 14, 15); }
+#undef KDA_FS4_BODY
+
 // A copy of x that the compiler cannot see through: values derived from it are
 // recomputed where they are used instead of being hoisted out of a loop and kept
 // live (or spilled) across it.

@@ -780,25 +780,31 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             // phase for the triangular solve of wave 0
             epilogue_stage(ch);
             // ---- 4. Gram blocks and T (waves 0, 1); X = V - Kbar S (all waves) -------------------
-            if (wave == 0 || (wave == 1 && qside)) {
-                // the Gram blocks and T gate the next barrier for the whole workgroup: their
-                // waves take issue priority over the other waves of their SIMDs meanwhile
-                __builtin_amdgcn_s_setprio(3);
-                const bool tw = wave == 0;
-                // Wave 0 forms its tile transposed, Kdiv Kbar^T, so that lane (lh, ln) holds row
-                // ln of A (columns 4lh .. 4lh+3); wave 1 forms P = Qbar Kdiv^T as it stands.  The
-                // beta values the solve needs are read before the products, off its chain.
-                float bs = 0.f;
-                float4 bc = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (tw) {
-                    const int x = opaque(lane);
-                    bs = BETA[x & 15];
-                    bc = *reinterpret_cast<const float4 *>(BETA + 4 * (x >> 4));
+            // X = V - Kbar S0 and O1 = Qbar S0, one K step of 32 channels at a time.  S0 is the B
+            // operand: K step s holds rows 32s + pi(slot), split into bf16 hi/lo right before use.
+            f32x4_t X = {0.f, 0.f, 0.f, 0.f}, O1 = {0.f, 0.f, 0.f, 0.f};
+            auto xo1_step = [&](int s) {
+                const int ka = ln * OPK + 32 * s + 8 * lh;
+                const uint4 kh = *reinterpret_cast<const uint4 *>(KLh + ka);
+                const uint4 kl_ = *reinterpret_cast<const uint4 *>(KLh + PL_CD + ka);
+                const float v8[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
+                                     S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
+                uint4 sh, sl;
+                split8_dot(v8, sh, sl);
+                X = mma3(kh, kl_, sh, sl, X);
+                if (qside) {
+                    const uint4 qh = *reinterpret_cast<const uint4 *>(QLh + ka);
+                    const uint4 ql_ = *reinterpret_cast<const uint4 *>(QLh + PL_CD + ka);
+                    O1 = mma3(qh, ql_, sh, sl, O1);
                 }
+            };
+            // The Gram tile of wave 0 (A, transposed: Kdiv Kbar^T, so that lane (lh, ln) holds
+            // row ln of A, columns 4lh .. 4lh+3) or wave 1 (P = Qbar Kdiv^T as it stands), with
+            // two independent accumulation chains (channels 0-63 and 64-127) that halve the
+            // dependent-MFMA latency on this critical path.
+            auto gram = [&](bool tw) {
                 const uint16_t *const Ap = tw ? (HEADG ? KLh : KRDh) : QLh;
                 const uint16_t *const Bp = tw ? KLh : (HEADG ? KLh : KRDh);  // k^ / Gamma, or k^ for the head gate
-                // two independent accumulation chains (channels 0-63 and 64-127) halve the
-                // dependent-MFMA latency on this critical path
                 f32x4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
                 for (int s = 0; s < D / 32; ++s) {
@@ -818,43 +824,66 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     for (int i = 0; i < 4; ++i)  // wave 0's tile is transposed: s = ln, j = 4lh + i
                         acc[i] *= __builtin_amdgcn_exp2f(fminf(tw ? g1 - gv[i] : gv[i] - g1, 0.0f));
                 }
-                if (tw) {
-                    // T = (I + A)^{-1} Diag(beta) by forward substitution in fp32.  Lane (c, r) =
-                    // 16c + r carries row r of X = (I + A)^{-1}, columns 4c .. 4c+3, and the whole
-                    // of row r of -A in registers: the lane's own four entries, A[r][4lh + i] =
-                    // beta_r Gram[r][4lh + i] for 4lh + i < r, gathered from the four 16-lane rows
-                    // of the wave with the gfx950 row swaps.  Step k then adds -A[r][k] X[k][j],
-                    // X[k][j] broadcast from lane k of the lane's own 16-lane row (DPP
-                    // row_newbcast), as one multiply-add per column: no LDS on the chain, and
-                    // each step depends on the previous one through one instruction.
-                    const int x = opaque(lane), r = x & 15, c = x >> 4;
-                    float na[4];
+                return acc;
+            };
+            if (wave == 0) {
+                // the Gram block and T gate the next barrier for the whole workgroup: this wave
+                // takes issue priority over the other wave of its SIMD meanwhile
+                __builtin_amdgcn_s_setprio(3);
+                // beta, read before the products, off the solve's chain
+                const int xb = opaque(lane);
+                const float bs = BETA[xb & 15];
+                const float4 bc = *reinterpret_cast<const float4 *>(BETA + 4 * (xb >> 4));
+                const f32x4_t acc = gram(true);
+                // T = (I + A)^{-1} Diag(beta) by forward substitution in fp32.  Lane (c, r) =
+                // 16c + r carries row r of X = (I + A)^{-1}, columns 4c .. 4c+3, and the whole
+                // of row r of -A in registers: the lane's own four entries, A[r][4lh + i] =
+                // beta_r Gram[r][4lh + i] for 4lh + i < r, gathered from the four 16-lane rows
+                // of the wave with the gfx950 row swaps.  Step k then adds -A[r][k] X[k][j],
+                // X[k][j] broadcast from lane k of the lane's own 16-lane row (DPP
+                // row_newbcast), as one multiply-add per column: no LDS on the chain, and
+                // each step depends on the previous one through one instruction.  This wave's
+                // own X / O1 products, independent of the solve, sit between its quarters and
+                // fill the gaps of its dependent chain.
+                const int x = opaque(lane), r = x & 15, c = x >> 4;
+                float na[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) na[i] = 4 * c + i < r ? -(acc[i] * bs) : 0.0f;
-                    float nA[C];
+                for (int i = 0; i < 4; ++i) na[i] = 4 * c + i < r ? -(acc[i] * bs) : 0.0f;
+                float nA[C];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        // permlane16_swap: rows 0, 1 get row 0 (first result) and row 1 (second),
-                        // rows 2, 3 get rows 2 and 3; permlane32_swap then spreads each to all rows
-                        const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(na[i]), __float_as_uint(na[i]), false, false);
-                        const auto q = __builtin_amdgcn_permlane32_swap(pr[0], pr[0], false, false);
-                        const auto w = __builtin_amdgcn_permlane32_swap(pr[1], pr[1], false, false);
-                        nA[i] = __uint_as_float(q[0]);       // row group 0: columns 0 .. 3
-                        nA[4 + i] = __uint_as_float(w[0]);   // row group 1
-                        nA[8 + i] = __uint_as_float(q[1]);   // row group 2
-                        nA[12 + i] = __uint_as_float(w[1]);  // row group 3
-                    }
-                    float xv[4];
+                for (int i = 0; i < 4; ++i) {
+                    // permlane16_swap: rows 0, 1 get row 0 (first result) and row 1 (second),
+                    // rows 2, 3 get rows 2 and 3; permlane32_swap then spreads each to all rows
+                    const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(na[i]), __float_as_uint(na[i]), false, false);
+                    const auto q = __builtin_amdgcn_permlane32_swap(pr[0], pr[0], false, false);
+                    const auto w = __builtin_amdgcn_permlane32_swap(pr[1], pr[1], false, false);
+                    nA[i] = __uint_as_float(q[0]);       // row group 0: columns 0 .. 3
+                    nA[4 + i] = __uint_as_float(w[0]);   // row group 1
+                    nA[8 + i] = __uint_as_float(q[1]);   // row group 2
+                    nA[12 + i] = __uint_as_float(w[1]);  // row group 3
+                }
+                float xv[4];
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) xv[m] = r == 4 * c + m ? 1.0f : 0.0f;
-                    forward_substitute16(xv, nA);
-                    const float tv[4] = {xv[0] * bc.x, xv[1] * bc.y, xv[2] * bc.z, xv[3] * bc.w};
-                    uint2 th, tl;
-                    split4_dot(tv, th, tl);
-                    // row r, columns 4c .. 4c+3: the A operand the state update reads in this lane
-                    *reinterpret_cast<uint2 *>(TMh + r * OPT + 4 * c) = th;
-                    *reinterpret_cast<uint2 *>(TMh + PL_CC + r * OPT + 4 * c) = tl;
-                } else {
+                for (int m = 0; m < 4; ++m) xv[m] = r == 4 * c + m ? 1.0f : 0.0f;
+                xo1_step(0);
+                forward_substitute4<0>(xv, nA);
+                xo1_step(1);
+                forward_substitute4<4>(xv, nA);
+                xo1_step(2);
+                forward_substitute4<8>(xv, nA);
+                xo1_step(3);
+                forward_substitute4<12>(xv, nA);
+                const float tv[4] = {xv[0] * bc.x, xv[1] * bc.y, xv[2] * bc.z, xv[3] * bc.w};
+                uint2 th, tl;
+                split4_dot(tv, th, tl);
+                // row r, columns 4c .. 4c+3: the A operand the state update reads in this lane
+                *reinterpret_cast<uint2 *>(TMh + r * OPT + 4 * c) = th;
+                *reinterpret_cast<uint2 *>(TMh + PL_CC + r * OPT + 4 * c) = tl;
+                __builtin_amdgcn_s_setprio(2);
+            } else {
+                if (wave == 1 && qside) {
+                    __builtin_amdgcn_s_setprio(3);
+                    const f32x4_t acc = gram(false);
                     const int y = opaque(lane), j = y & 15, lg = y >> 4;
                     const int r = 4 * lg;
                     const float pv[4] = {j <= r ? acc[0] : 0.0f, j <= r + 1 ? acc[1] : 0.0f,
@@ -863,27 +892,10 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                     split4_dot(pv, ph, pl);
                     store_halves(PMh + r * OPT + j, OPT, ph);
                     store_halves(PMh + PL_CC + r * OPT + j, OPT, pl);
+                    __builtin_amdgcn_s_setprio(2);
                 }
-                __builtin_amdgcn_s_setprio(2);
-            }
-            // X = V - Kbar S0 and O1 = Qbar S0.  S0 is the B operand: K step s holds rows
-            // 32s + pi(slot), split into bf16 hi/lo right before use.
-            f32x4_t X = {0.f, 0.f, 0.f, 0.f}, O1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int ka = ln * OPK + 32 * s + 8 * lh;
-                const uint4 kh = *reinterpret_cast<const uint4 *>(KLh + ka);
-                const uint4 kl_ = *reinterpret_cast<const uint4 *>(KLh + PL_CD + ka);
-                const float v8[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
-                                     S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
-                uint4 sh, sl;
-                split8_dot(v8, sh, sl);
-                X = mma3(kh, kl_, sh, sl, X);
-                if (qside) {
-                    const uint4 qh = *reinterpret_cast<const uint4 *>(QLh + ka);
-                    const uint4 ql_ = *reinterpret_cast<const uint4 *>(QLh + PL_CD + ka);
-                    O1 = mma3(qh, ql_, sh, sl, O1);
-                }
+                for (int s = 0; s < 4; ++s) xo1_step(s);
             }
             if (HEADG) {  // the row scales Gamma of Kbar = Diag(Gamma) K^ and Qbar = Diag(Gamma) Q^
                 const float4 gr = *reinterpret_cast<const float4 *>(GH + 4 * lh);

@@ -72,6 +72,13 @@ def prefill_mfma_flops(T: int, H: int, C: int = 16) -> int:
     return T * H * (6 * D * D + 8 * C * D)
 
 
+def prefill_mfma_flops_ref(T: int, H: int, C: int = 64) -> int:
+    """The reference matrix-core count of the chunked form at 64-token chunks with 16-token
+    triangles, 6 d^2 + 5 (C + 16) d = 149,504 per token-head: the figure the work was
+    scoped with, reported beside the kernel's own count for comparison."""
+    return T * H * (6 * D * D + 5 * (C + 16) * D)
+
+
 def measure_peaks(dev, stream, log, gib: int = 2) -> dict:
     """This GPU's measured ceilings (libkda_peaks.so): a streaming copy of `gib` GiB (bytes
     read + written / time), a read stream of the same size, and a loop of independent
@@ -640,6 +647,8 @@ def main() -> int:
                     "algorithmic_bytes": pb, "mfma_flops_c16": pf,
                     "mfma_tflops": pf / (pre_mean * 1e-3) / 1e12,
                     "mfma_frac_of_peak": pf / (pre_mean * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                    "mfma_flops_ref_c64": prefill_mfma_flops_ref(T, H),
+                    "mfma_frac_of_peak_ref_c64": prefill_mfma_flops_ref(T, H) / (pre_mean * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                     "hbm_roofline_tokens_per_s": T / (pb / (HBM_PEAK_GBPS * 1e9))},
         "decode": {"ms": dec_mean, "ms_median": dec_med, "state_GBps": dec_state_gbps,
                    "algorithmic_bytes": db, "GBps": dec_gbps,

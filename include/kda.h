@@ -119,8 +119,8 @@ typedef int32_t kda_status;
  * section "Channel-wise decay, and the floor K3 puts under it"): log_alpha is
  * [T][H].  The decay factors leave the channel contractions, so the kernel forms
  * fewer operand planes and exponentials and spends part of the saving on the row
- * scales of the products: at 4 x 4096 tokens x 96 heads it measured 3% faster than the
- * channel gate (1.25 against 1.29 ms). */
+ * scales of the products: at 4 x 4096 tokens x 96 heads it measured 5% faster than the
+ * channel gate (1.24 against 1.30 ms). */
 #define KDA_GATE_HEAD 2
 /* LOWRANK_SOFTPLUS: Kimi Linear's gate, formed in the kernels from the same factors as
  * LOWRANK: log alpha = -e^{A_h} softplus(z_down W_up^T + b), which has no floor

@@ -312,6 +312,23 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     const char *g_base = static_cast<const char *>(p.epilogue ? p.g : p.q) + first * sizeof(IO);
     char *o_base = static_cast<char *>(p.o) + first * sizeof(OUT);
 
+    // Low-rank gate: z_down rows of a chunk (fetched with the chunk's q, k, v rows a whole
+    // chunk ahead, parked in ZL when the chunk starts) and this lane's W_up operand (the B
+    // operand of z_down W_up^T for the channels 16 wave .. 16 wave + 15, fetched at the end
+    // of the previous chunk's state update, so that the staging phase covers its latency).
+    const int rank = p.gate_rank;
+    const int zsteps = rank / 32;
+    uint2 zr = make_uint2(0u, 0u);
+    uint4 wb[4];
+    const char *z_base = LOWRANK ? static_cast<const char *>(p.gate_z) + static_cast<size_t>(t0) * rank * 2 : nullptr;
+    auto load_z = [&](int c) {
+        const int x = opaque(tid), xt = x >> 5, xc = (x & 31) * 4;
+        const int r0 = c * C, nrow = min(L, r0 + C) - r0;
+        const __amdgpu_buffer_rsrc_t v = rows_view(z_base + static_cast<size_t>(r0) * rank * 2, nrow, rank * 2, rank * 2);
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t z = __builtin_amdgcn_raw_buffer_load_b64(v, static_cast<uint32_t>(xt * rank + xc) * 2u, 0, 0);
+        zr = make_uint2(z[0], z[1]);  // (lanes past the rank are not parked)
+    };
     // Per-thread offsets of the prefetches are rebuilt from an opaque copy of the thread
     // index at each use rather than kept live across the loop: a spilled offset would
     // be reloaded with a wait that also drains the prefetches in flight.
@@ -331,22 +348,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
                                         static_cast<uint32_t>(xt) * rowb_f + xc * 4u);
         bet = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
             rows_view(beta_base + static_cast<size_t>(r0) * H * 4, nrow, H * 4, 4), static_cast<uint32_t>(xt * H) * 4u, 0, 0));
-    };
-    // Low-rank gate: z_down rows of a chunk (one chunk ahead, parked in ZL before the
-    // chunk starts) and this lane's W_up operand (the B operand of z_down W_up^T for
-    // the channels 16 wave .. 16 wave + 15, loaded during the previous epilogue).
-    const int rank = p.gate_rank;
-    const int zsteps = rank / 32;
-    uint2 zr = make_uint2(0u, 0u);
-    uint4 wb[4];
-    const char *z_base = LOWRANK ? static_cast<const char *>(p.gate_z) + static_cast<size_t>(t0) * rank * 2 : nullptr;
-    auto load_z = [&](int c) {
-        const int x = opaque(tid), xt = x >> 5, xc = (x & 31) * 4;
-        const int r0 = c * C, nrow = min(L, r0 + C) - r0;
-        const __amdgpu_buffer_rsrc_t v = rows_view(z_base + static_cast<size_t>(r0) * rank * 2, nrow, rank * 2, rank * 2);
-        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-        const u32x2_t z = __builtin_amdgcn_raw_buffer_load_b64(v, static_cast<uint32_t>(xt * rank + xc) * 2u, 0, 0);
-        zr = xc < rank ? make_uint2(z[0], z[1]) : make_uint2(0u, 0u);
+        if (LOWRANK) load_z(c);
     };
     auto park_z = [&]() {
         const int x = opaque(tid), xt = x >> 5, xc = (x & 31) * 4;
@@ -436,7 +438,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     };
     auto next_loads = [&](int ch) {
         load_gate(ch, true);
-        if (LOWRANK) load_z(ch + 1);
+        if (LOWRANK) load_w();  // this lane's W_up operand, for the next chunk's gate
     };
     if (p.prologue && tid < 3 * CONV_HIST * 16) {
         // history of the first chunk: the given conv cache (oldest first) or zeros
@@ -459,10 +461,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         // wait for the rows at the top of the loop need not cover the output store
         store_dummy();
         load_gate(0, false);
-        if (LOWRANK) {
-            load_z(0);
-            load_w();
-        }
+        if (LOWRANK) load_w();
     }
     // this thread's staged row (position et) and the same row three positions earlier
     float *const raw_t = RAW + ((CONV_HIST + et) * 3) * D + ec0;
@@ -495,7 +494,6 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         // for every memory operation in flight)
         if ((tid & 31) == 0) BETA[opaque(tid) >> 5] = p.beta_logit ? sigmoidf_(bet) : bet;
         if (WIDE && tid == 0) *FLAG = 0;
-        if (LOWRANK) load_w();  // this lane's W_up operand, used right after the barrier
         // the next chunk's rows: a whole chunk of work hides their latency (past the last
         // chunk the views are empty: zeros, no memory access, and the same count of memory
         // operations on every path, so that later waits stay exact)
@@ -510,6 +508,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
         // vector-heavy phases, which fill the gaps; with the arbiter's default (older waves
         // first) one workgroup of the pair ran far behind the other.
         __builtin_amdgcn_s_setprio(1);
+        f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
         if (LOWRANK) {
             // log2(alpha) = -5 log2(e) sigmoid(e^{A_h} (z_down W_up^T + b)) for the chunk's
             // tokens (rows) and this wave's 16 channels (columns), on the matrix cores (the
@@ -519,43 +518,11 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
             // that they do not decay the carried state.
             // (LDS addresses from an opaque lane index, as elsewhere: a spilled address costs a
             // reload that waits for every memory operation in flight)
-            const int y = opaque(lane), yl = y & 15, yh = y >> 4, ycol = wave * 16 + yl;
-            f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
-            const uint16_t *const zrow = ZL + yl * ZPK + 8 * yh;
+            const int y = opaque(lane);
+            const uint16_t *const zrow = ZL + (y & 15) * ZPK + 8 * (y >> 4);
 #pragma unroll
             for (int st = 0; st < 4; ++st)
                 if (st < zsteps) zacc = mma(*reinterpret_cast<const uint4 *>(zrow + 32 * st), wb[st], zacc);
-            float run[4];
-            float acc_sum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float la2;
-                if (SOFTPLUS) {
-                    // -e^{A_h} softplus(u) log2(e) = -e^{A_h} log2(1 + 2^t), t = u log2(e),
-                    // as max(t, 0) + log2(1 + 2^-|t|) so that 2^t never overflows
-                    const float t = fmaf(zacc[i], LOG2E, gbias);
-                    la2 = -gscale * (fmaxf(t, 0.0f) + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-fabsf(t))));
-                } else {
-                    const float t = fmaf(zacc[i], gscale, gbias);  // e^{A_h} (z + b) log2(e)
-                    la2 = (-5.0f * LOG2E) * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
-                }
-                la2 = r0 + 4 * yh + i < L ? la2 : 0.0f;
-                if (WIDE) AL[(4 * yh + i) * D + ycol] = __builtin_amdgcn_exp2f(la2);
-                acc_sum += la2;
-                run[i] = acc_sum;
-            }
-            float x1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((y - 16) * 4, __builtin_bit_cast(int, acc_sum)));
-            x1 = acc_sum + (yh >= 1 ? x1 : 0.0f);
-            float x2 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((y - 32) * 4, __builtin_bit_cast(int, x1)));
-            x2 = x1 + (yh >= 2 ? x2 : 0.0f);
-            const float before = x2 - acc_sum;  // sum over the rows of the earlier row groups
-            float *const larow = LA + 4 * yh * D + ycol;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) larow[i * D] = run[i] + before;
-            if (yh == 3) {
-                EGC[ycol] = __builtin_amdgcn_exp2f(run[3] + before);
-                if (WIDE && run[3] + before < -WIDE_LOG2) *FLAG = 1;
-            }
         }
         float xq[4], xk[4], xv[4];
         {
@@ -617,6 +584,42 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) xq[e] = xk[e] = xv[e] = 0.0f;
                 }
+            }
+        }
+        if (LOWRANK) {
+            // the rest of the gate, after the convolution, which hides the latency of the
+            // z_down W_up^T products
+            const int y = opaque(lane), yl = y & 15, yh = y >> 4, ycol = wave * 16 + yl;
+            float run[4];
+            float acc_sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float la2;
+                if (SOFTPLUS) {
+                    // -e^{A_h} softplus(u) log2(e) = -e^{A_h} log2(1 + 2^t), t = u log2(e),
+                    // as max(t, 0) + log2(1 + 2^-|t|) so that 2^t never overflows
+                    const float t = fmaf(zacc[i], LOG2E, gbias);
+                    la2 = -gscale * (fmaxf(t, 0.0f) + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-fabsf(t))));
+                } else {
+                    const float t = fmaf(zacc[i], gscale, gbias);  // e^{A_h} (z + b) log2(e)
+                    la2 = (-5.0f * LOG2E) * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
+                }
+                la2 = r0 + 4 * yh + i < L ? la2 : 0.0f;
+                if (WIDE) AL[(4 * yh + i) * D + ycol] = __builtin_amdgcn_exp2f(la2);
+                acc_sum += la2;
+                run[i] = acc_sum;
+            }
+            float x1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((y - 16) * 4, __builtin_bit_cast(int, acc_sum)));
+            x1 = acc_sum + (yh >= 1 ? x1 : 0.0f);
+            float x2 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((y - 32) * 4, __builtin_bit_cast(int, x1)));
+            x2 = x1 + (yh >= 2 ? x2 : 0.0f);
+            const float before = x2 - acc_sum;  // sum over the rows of the earlier row groups
+            float *const larow = LA + 4 * yh * D + ycol;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) larow[i * D] = run[i] + before;
+            if (yh == 3) {
+                EGC[ycol] = __builtin_amdgcn_exp2f(run[3] + before);
+                if (WIDE && run[3] + before < -WIDE_LOG2) *FLAG = 1;
             }
         }
         if (SEG && role == SEG_M) {  // the transition matrix: the recurrence with v = 0

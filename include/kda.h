@@ -42,6 +42,11 @@
  *    reentrant and thread-safe; results are valid once the stream reaches
  *    the call.  Host-side validation failures return an error status and
  *    enqueue nothing.  No call aborts or throws.
+ *  - The calls enqueue kernel launches only (no memset, copy, allocation or
+ *    host synchronisation), so a call can be captured in a HIP graph and the
+ *    graph replayed; the buffers it names are then fixed.  kda_prefill_no_alloc
+ *    resolves its per-GPU scratch on its first call on a GPU: make that first
+ *    call outside a capture.
  *  - Initialisation order: the library shares the process's HIP runtime and
  *    registers its kernels when it is loaded.  Initialise the runtime first
  *    (any HIP call that touches the device, e.g. hipSetDevice or hipFree(0),

@@ -431,6 +431,46 @@ def run_serving_workloads(kda, dev, stream, log, H=96, B=256, drafts=4) -> dict:
                                 "verified_tokens_per_s": T / (vms * 1e-3)}
     log(f"speculative round: verify {T} tokens {vms:.3f} ms, replay {Ta} tokens {rms_:.3f} ms")
     del pool, conv
+
+    # Small batches, where a step's launch costs as much as its state traffic: `steps`
+    # decode steps launched one by one, against the same steps captured once in a HIP graph.
+    steps = 32
+    for Bs in (1, 8):
+        pool_s = normal(Bs, H, D, D, std=0.02, dtype=torch.float32)
+        conv_s = normal(Bs, 3, 3, H * D)
+        sq, sk, sv, sg = (normal(Bs, H, D) for _ in range(4))
+        sla, sbeta = gates(Bs, H)
+        so = torch.empty((Bs, H, D), dtype=bf, device=dev)
+
+        def small_step(s):
+            kda.decode_step(sq, sk, sv, sla, sbeta, pool_s, g=sg, conv_w=cw, conv_state=conv_s, o=so,
+                            cfg=cfg, stream=s)
+
+        def eager_loop():
+            for _ in range(steps):
+                small_step(stream)
+
+        warm_up(eager_loop, 3)
+        ems, _ = time_events(eager_loop, 10, stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):  # the binding launches on the capturing stream
+            for _ in range(steps):
+                small_step(None)
+
+        def graph_loop():
+            with torch.cuda.stream(stream):
+                graph.replay()
+
+        warm_up(graph_loop, 3)
+        gms, _ = time_events(graph_loop, 10, stream)
+        state_bytes = 2 * Bs * H * D * D * 4
+        out[f"decode_{Bs}x{H}_graph"] = {
+            "requests": Bs, "heads": H, "steps": steps,
+            "eager_us_per_step": ems * 1e3 / steps, "graph_us_per_step": gms * 1e3 / steps,
+            "graph_state_GBps": state_bytes * steps / (gms * 1e-3) / 1e9}
+        log(f"decode {Bs} x {H}: {ems * 1e3 / steps:.1f} us per step launched one by one, "
+            f"{gms * 1e3 / steps:.1f} us in a HIP graph of {steps} steps")
+        del graph, pool_s, conv_s
     torch.cuda.empty_cache()
     return out
 

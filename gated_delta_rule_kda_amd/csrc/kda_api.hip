@@ -114,36 +114,41 @@ bool scan_supported(const kda_config *cfg) {
            (cfg->gate == KDA_GATE_LOG_ALPHA || cfg->gate == KDA_GATE_LOWRANK || cfg->gate == KDA_GATE_HEAD);
 }
 
-// Segment length (tokens, a multiple of the 16-token chunk) and table slots of the
-// segmented prefill, at least 2048 tokens per segment when the choice is AUTO's (64 when
-// asked for by name).  P segments per sequence rerun P - 1 of them in the last pass; P - 1
-// = floor(2 CUs / items) fills the two workgroup slots of every CU once there, and one
-// more segment would need a second round (131072 tokens: 96 heads, P = 6 took 23.9 ms,
+// Segment length (tokens, a multiple of the 16-token chunk, at least 64) and table slots
+// of the segmented prefill.  P segments per sequence rerun P - 1 of them in the last pass;
+// P - 1 = floor(2 CUs / items) fills the two workgroup slots of every CU once there, and
+// one more segment would need a second round (131072 tokens: 96 heads, P = 6 took 23.9 ms,
 // P = 5 25.6 and P = 7 29.9; 12 heads, P = 43 took 3.45 ms and P = 42 3.8).
 struct ScanPlan {
     int32_t seg_tokens, slots;
 };
-ScanPlan scan_plan(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens, bool named) {
+ScanPlan scan_plan(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
     const int64_t items = static_cast<int64_t>(num_seqs) * cfg->num_heads;
     const int64_t per_seq = std::max<int64_t>(2, 1 + 2 * device_cu_count() / std::max<int64_t>(items, 1));
     const int64_t avg = (total_tokens + num_seqs - 1) / num_seqs;
     int64_t seg = ((avg + per_seq - 1) / per_seq + 15) / 16 * 16;
-    seg = std::max<int64_t>(seg, named ? 64 : 2048);
+    seg = std::max<int64_t>(seg, 64);
     seg = std::min<int64_t>(seg, 1LL << 30);
     const int64_t slots = num_seqs + (total_tokens + seg - 1) / seg;
     return {static_cast<int32_t>(seg), static_cast<int32_t>(std::min<int64_t>(slots, 0x7fffffffLL))};
 }
 
-int32_t resolve_algo(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens) {
+// AUTO and CHUNKED: the throughput kernel, or the segmented prefill when one sequential
+// pass would leave most CUs idle (scan_ok false: never, for the no-allocation entry point,
+// whose scratch cannot hold the segment matrices).  Measured with the full layer on bf16
+// inputs: at most 3/8 as many (sequence, head) items as CUs, over sequences averaging 1024
+// tokens or more, gain 1.1x (96 items of 4096 tokens: 0.92 -> 0.83 ms) to 4.5x (12 items
+// of 8192: 1.79 -> 0.40 ms), while 128 items of 4096 tokens lose 5-10%; with fewer items
+// than CUs, sequences averaging 16384 tokens or more gain (1 x 131072 x 96: 27.8 -> 20.4 ms).
+int32_t resolve_algo(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens, bool scan_ok = true) {
     int algo = cfg->algo;
     if (algo == KDA_ALGO_AUTO) algo = cfg->io_dtype == KDA_DTYPE_BF16 ? KDA_ALGO_CHUNKED : KDA_ALGO_RECURRENT;
     if (algo == KDA_ALGO_CHUNKED) {
-        // few (sequence, head) items over long sequences leave most CUs idle in one
-        // sequential pass: split the sequences (one 131072-token sequence x 96 heads)
         const int64_t items = static_cast<int64_t>(num_seqs) * cfg->num_heads;
-        algo = scan_supported(cfg) && items < device_cu_count() && total_tokens >= 16384LL * num_seqs
-                   ? KDA_ALGO_CHUNKED_SCAN
-                   : KDA_ALGO_CHUNKED_THROUGHPUT;
+        const bool few = items <= 3 * device_cu_count() / 8 && total_tokens >= 1024LL * num_seqs;
+        const bool long_seqs = items < device_cu_count() && total_tokens >= 16384LL * num_seqs;
+        algo = scan_ok && scan_supported(cfg) && (few || long_seqs) ? KDA_ALGO_CHUNKED_SCAN
+                                                                    : KDA_ALGO_CHUNKED_THROUGHPUT;
     }
     return algo;
 }
@@ -161,7 +166,7 @@ bool supported(const kda_config *cfg, int32_t algo) {
 
 size_t workspace_bytes(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens, int32_t algo) {
     if (algo != KDA_ALGO_CHUNKED_SCAN) return order_workspace_bytes(num_seqs);
-    const ScanPlan sp = scan_plan(cfg, num_seqs, total_tokens, cfg->algo == KDA_ALGO_CHUNKED_SCAN);
+    const ScanPlan sp = scan_plan(cfg, num_seqs, total_tokens);
     return scan_workspace_bytes(cfg->num_heads, num_seqs, sp.slots);
 }
 
@@ -221,9 +226,10 @@ kda_status kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs, i
 namespace {
 
 // Host validation shared by both prefill entry points: everything but the workspace.
-// On success *algo is the algorithm that will run and *need the workspace bytes it uses.
+// On success *algo is the algorithm that will run (AUTO resolved as resolve_algo does with
+// scan_ok) and *need the workspace bytes it uses.
 kda_status check_prefill(const kda_config *cfg, const kda_prefill_args *a, const void *workspace, int32_t *algo,
-                         size_t *need) {
+                         size_t *need, bool scan_ok) {
     kda_status st = check_config(cfg);
     if (st != KDA_OK) return st;
     if (!a || a->num_seqs <= 0 || a->total_tokens < 0) return KDA_ERR_INVALID_ARGUMENT;
@@ -239,7 +245,7 @@ kda_status check_prefill(const kda_config *cfg, const kda_prefill_args *a, const
         !ok_ptr(a->state_out, false) || !ok_ptr(workspace, false) ||
         !ok_ptr(a->state_in_slots, false) || !ok_ptr(a->state_out_slots, false))
         return KDA_ERR_INVALID_ARGUMENT;
-    *algo = resolve_algo(cfg, a->num_seqs, a->total_tokens);
+    *algo = resolve_algo(cfg, a->num_seqs, a->total_tokens, scan_ok);
     *need = workspace_bytes(cfg, a->num_seqs, a->total_tokens, *algo);
     return KDA_OK;
 }
@@ -249,10 +255,10 @@ kda_status check_prefill(const kda_config *cfg, const kda_prefill_args *a, const
 // resolved algorithm needs (or NULL where one is needed) is refused, then a configuration
 // the algorithm does not run, and only then is anything enqueued.
 kda_status prefill_with(const kda_config *cfg, const kda_prefill_args *a, void *hip_stream, void *workspace,
-                        size_t ws_bytes) {
+                        size_t ws_bytes, bool scan_ok) {
     int32_t algo = 0;
     size_t need = 0;
-    kda_status st = check_prefill(cfg, a, workspace, &algo, &need);
+    kda_status st = check_prefill(cfg, a, workspace, &algo, &need, scan_ok);
     if (st != KDA_OK) return st;
     if (need > 0 && (!workspace || ws_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (!supported(cfg, algo)) return KDA_ERR_UNSUPPORTED;
@@ -289,7 +295,7 @@ kda_status prefill_with(const kda_config *cfg, const kda_prefill_args *a, void *
                 cfg->out_dtype, algo, cfg->prologue, cfg->epilogue);
     hipError_t e;
     if (algo == KDA_ALGO_CHUNKED_SCAN) {
-        const ScanPlan sp = scan_plan(cfg, a->num_seqs, a->total_tokens, cfg->algo == KDA_ALGO_CHUNKED_SCAN);
+        const ScanPlan sp = scan_plan(cfg, a->num_seqs, a->total_tokens);
         if (trace_enabled()) fprintf(stderr, "[kda] scan: %d-token segments, %d slots\n", sp.seg_tokens, sp.slots);
         e = launch_chunked_scan(p, cfg->out_dtype, a->num_seqs, sp.seg_tokens, sp.slots, workspace, s);
     } else if (algo == KDA_ALGO_CHUNKED_THROUGHPUT)
@@ -334,20 +340,20 @@ kda_status device_scratch(hipStream_t s, void **out) {
 extern "C" {
 
 kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *a, void *hip_stream) {
-    return prefill_with(cfg, a, hip_stream, a ? a->workspace : nullptr, a ? a->workspace_bytes : 0);
+    return prefill_with(cfg, a, hip_stream, a ? a->workspace : nullptr, a ? a->workspace_bytes : 0, true);
 }
 
 kda_status kda_prefill_no_alloc(const kda_config *cfg, const kda_prefill_args *a, void *hip_stream) {
     int32_t algo = 0;
     size_t need = 0;
-    kda_status st = check_prefill(cfg, a, nullptr, &algo, &need);
+    kda_status st = check_prefill(cfg, a, nullptr, &algo, &need, false);
     if (st != KDA_OK) return st;
     if (need > KDA_NO_ALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (!supported(cfg, algo)) return KDA_ERR_UNSUPPORTED;
     void *ws = nullptr;
     st = device_scratch(static_cast<hipStream_t>(hip_stream), &ws);
     if (st != KDA_OK) return st;
-    return prefill_with(cfg, a, hip_stream, ws, KDA_NO_ALLOC_SCRATCH_BYTES);
+    return prefill_with(cfg, a, hip_stream, ws, KDA_NO_ALLOC_SCRATCH_BYTES, false);
 }
 
 kda_status kda_decode_step(const kda_config *cfg, const kda_decode_args *a, void *hip_stream) {

@@ -104,11 +104,14 @@ typedef int32_t kda_status;
  * state.  A scan S_{p+1} = M_p S_p + B_p over the segments then gives every
  * segment's entering state, and segments 1 .. P-1 run again from it to produce
  * their outputs.  About 2.6x the arithmetic of one pass, for up to P-fold
- * parallelism: AUTO takes it for bf16 inputs when the (sequence, head) items are
- * fewer than the compute units and sequences average 16384 tokens or more, with
- * P segments per sequence such that the rerun of P - 1 of them fills two workgroup
- * slots on each compute unit.  bf16 io and the LOG_ALPHA, LOWRANK and
- * HEAD gates only; its M and B matrices live in the workspace. */
+ * parallelism, with P segments per sequence (at least 64 tokens each) such that the
+ * rerun of P - 1 of them fills two workgroup slots on each compute unit.  AUTO and
+ * CHUNKED take it for bf16 inputs when one pass would leave most compute units idle:
+ * at most 3/8 as many (sequence, head) items as compute units over sequences averaging
+ * 1024 tokens or more (12 items of 8192 tokens: 4.5x faster; 96 items of 4096: 1.1x),
+ * or fewer items than compute units over sequences averaging 16384 tokens or more.
+ * bf16 io and the LOG_ALPHA, LOWRANK and HEAD gates only; its M and B matrices live in
+ * the workspace. */
 #define KDA_ALGO_CHUNKED_SCAN 5
 
 /* Where the decay comes from ("Kimi K3 - KDA layer" step list: z_down = x W_down,
@@ -230,9 +233,10 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *args, void
  * until the process ends; no call here allocates or frees memory.  Limit: configurations
  * whose workspace (kda_prefill_workspace_size) exceeds KDA_NO_ALLOC_SCRATCH_BYTES return
  * KDA_ERR_WORKSPACE_TOO_SMALL and enqueue nothing: the segmented prefill
- * (KDA_ALGO_CHUNKED_SCAN) never fits, so choose KDA_ALGO_CHUNKED_THROUGHPUT or call
- * kda_prefill with a workspace for a few very long sequences; the other algorithms need
- * at most 32 KiB (the longest-first order of up to 8192 sequences).  Every call on one
+ * (KDA_ALGO_CHUNKED_SCAN) never fits, so here AUTO and CHUNKED never select it (they
+ * run the throughput kernel where kda_prefill would split the sequences), and naming
+ * it is refused; the other algorithms need at most 32 KiB (the longest-first order of
+ * up to 8192 sequences).  Every call on one
  * GPU shares that GPU's array, and the kernels overwrite all of it that they read, so no
  * state carries from one call to the next; calls that overlap in time on one GPU (on
  * different streams, or from different threads without ordering) race on the array and
@@ -243,7 +247,8 @@ kda_status kda_prefill(const kda_config *cfg, const kda_prefill_args *args, void
 kda_status kda_prefill_no_alloc(const kda_config *cfg, const kda_prefill_args *args, void *hip_stream);
 
 /* The KDA_ALGO_* that kda_prefill runs for this configuration, num_seqs sequences
- * and total_tokens tokens on the current device (AUTO and CHUNKED resolved), or -1
+ * and total_tokens tokens on the current device (AUTO and CHUNKED resolved; the
+ * no-allocation entry point runs CHUNKED_THROUGHPUT where this says CHUNKED_SCAN), or -1
  * when the configuration is invalid, num_seqs <= 0 or total_tokens < 0.  Host only;
  * enqueues nothing. */
 int32_t kda_prefill_resolved_algo(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens);

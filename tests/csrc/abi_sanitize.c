@@ -127,8 +127,9 @@ int main(void) {
     EXPECT(kda_prefill(&c, &a, NULL), KDA_ERR_WORKSPACE_TOO_SMALL);
     c.gate_rank = 48; EXPECT(kda_prefill(&c, &a, NULL), KDA_ERR_UNSUPPORTED);
 
-    /* the no-allocation entry point validates the same way, before any HIP call */
-    kda_config_init(&c, 96);
+    /* the no-allocation entry point validates the same way, before any HIP call (the
+       segmented prefill, named, needs more than its scratch; AUTO never selects it there) */
+    kda_config_init(&c, 96); c.algo = KDA_ALGO_CHUNKED_SCAN;
     a = prefill_args(); a.num_seqs = 1; a.total_tokens = 131072; a.workspace = NULL; a.workspace_bytes = 0;
     EXPECT(kda_prefill_no_alloc(&c, &a, NULL), KDA_ERR_WORKSPACE_TOO_SMALL);
     kda_config_init(&c, 4);

@@ -214,15 +214,14 @@ def test_decode_rejects_bad_arguments():
 
 def test_no_alloc_validation():
     """kda_prefill_no_alloc validates like kda_prefill and ignores the caller's workspace;
-    a configuration whose workspace exceeds the static scratch (the segmented prefill) is
-    refused before any HIP call."""
+    a configuration whose workspace exceeds the static scratch (the segmented prefill, when
+    named: AUTO never selects it here) is refused before any HIP call.  Only refusals are
+    exercised: these arguments hold no device memory."""
     L = kda.lib()
 
     def na(cfg, a):
         return L.kda_prefill_no_alloc(ctypes.byref(cfg), ctypes.byref(a), None)
 
-    big = dict(num_seqs=1, total_tokens=131072, workspace=None, workspace_bytes=0)
-    assert na(kda.config(96), _args(**big)) == kda.ERR_WORKSPACE_TOO_SMALL  # AUTO -> scan
     assert na(kda.config(4, algo="chunked_scan"), _args(num_seqs=3, total_tokens=300)) == kda.ERR_WORKSPACE_TOO_SMALL
     assert na(kda.config(4), _args(q=None)) == kda.ERR_INVALID_ARGUMENT
     assert na(kda.config(4), _args(num_seqs=0)) == kda.ERR_INVALID_ARGUMENT
@@ -249,13 +248,19 @@ def test_resolved_algo():
 
 
 def test_scan_selection_and_workspace():
-    """AUTO splits long sequences when (sequence, head) items are fewer than compute units
-    (256 when sized without a device); the workspace then holds two 64 KiB matrices per
-    (segment slot, head)."""
+    """AUTO splits the sequences when one pass would leave most compute units idle (256
+    when sized without a device): at most 96 (sequence, head) items over sequences
+    averaging 1024 tokens or more, or fewer than 256 items over sequences averaging 16384;
+    the workspace then holds two 64 KiB matrices per (segment slot, head)."""
     c = kda.config(96)
     assert kda.resolved_algo(c, 1, 131072) == "chunked_scan"
     assert kda.resolved_algo(c, 4, 16384) == "chunked_throughput"     # 384 items
-    assert kda.resolved_algo(c, 1, 8192) == "chunked_throughput"      # too short
+    assert kda.resolved_algo(c, 1, 8192) == "chunked_scan"            # 96 items
+    assert kda.resolved_algo(c, 1, 1023) == "chunked_throughput"      # too short
+    assert kda.resolved_algo(kda.config(12), 4, 4 * 4096) == "chunked_scan"   # 48 items
+    assert kda.resolved_algo(kda.config(128), 1, 8192) == "chunked_throughput"  # 128 items
+    assert kda.resolved_algo(kda.config(128), 1, 16384) == "chunked_scan"       # long
+    assert kda.resolved_algo(kda.config(96, gate="head"), 1, 8192) == "chunked_scan"
     assert kda.resolved_algo(kda.config(96, io_dtype="f32"), 1, 131072) == "recurrent"
     assert kda.resolved_algo(kda.config(96, gate="lowrank_softplus"), 1, 131072) == "chunked_throughput"
     assert kda.resolved_algo(kda.config(96, algo="chunked_throughput"), 1, 131072) == "chunked_throughput"

@@ -151,3 +151,32 @@ def test_scan_tp8_shape_sampled():
     say(f"  heads {heads}: o err {eo:.2e}  S err {es:.2e}")
     assert eo <= TOL and es <= TOL
     assert np.isfinite(g["o"]).all()
+
+
+def test_auto_splits_few_items():
+    """Few (sequence, head) items over moderate lengths (2 sequences of 1536 and 1200
+    tokens x 4 heads, 8 items): AUTO takes the segmented prefill, which meets the oracle;
+    the no-allocation entry point, whose scratch cannot hold the segment matrices, runs the
+    throughput kernel instead, bit for bit as kda_prefill does when that kernel is named."""
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    H, lens = 4, [1536, 1200]
+    inp = W.gen_prefill(W.PrefillSpec(lens=lens, heads=H, state_std=0.05, conv_in=True, decay="slow", seed=125))
+    assert kda.resolved_algo(kda.config(H), len(lens), sum(lens)) == "chunked_scan"
+    say("auto on 8 items: scan")
+    g = gpu_prefill(inp, algo="auto")
+    r = oracle_prefill(inp)
+    assert err(g["o"], r["o"]) <= TOL and err(g["state"], r["state"]) <= TOL
+    assert np.array_equal(g["conv"], r["conv"])
+    bf, f32 = torch.bfloat16, torch.float32
+    args = (to_dev(inp["q"], bf), to_dev(inp["k"], bf), to_dev(inp["v"], bf), to_dev(inp["log_alpha"], f32),
+            to_dev(inp["beta"], f32), to_dev(inp["cu_seqlens"].astype(np.int32), torch.int32))
+    kw = dict(g=to_dev(inp["g"], bf), conv_w=to_dev(inp["conv_w"], f32), conv_in=to_dev(inp["conv_in"], bf),
+              state_in=to_dev(inp["state_in"], f32))
+    say("auto on 8 items: no-alloc entry point")
+    na = kda.prefill(*args, **kw, cfg=kda.config(H, out_dtype="f32"), no_alloc=True)
+    tp = kda.prefill(*args, **kw, cfg=kda.config(H, out_dtype="f32", algo="chunked_throughput"))
+    torch.cuda.synchronize()
+    for a, b in zip(na, tp):
+        assert torch.equal(a, b)
+    assert err(to_np(na[0]), r["o"]) <= TOL

@@ -262,6 +262,13 @@ kda_status prefill_with(const kda_config *cfg, const kda_prefill_args *a, void *
     if (st != KDA_OK) return st;
     if (need > 0 && (!workspace || ws_bytes < need)) return KDA_ERR_WORKSPACE_TOO_SMALL;
     if (!supported(cfg, algo)) return KDA_ERR_UNSUPPORTED;
+    if (algo == KDA_ALGO_CHUNKED_SCAN) {
+        // the segmented prefill's grids, 2 x slots x H workgroups for the first pass and
+        // 8 x N x H for the scan, must fit one 32-bit grid dimension
+        const ScanPlan sp = scan_plan(cfg, a->num_seqs, a->total_tokens);
+        if (2LL * sp.slots * cfg->num_heads > 0x7fffffffLL || 8LL * a->num_seqs * cfg->num_heads > 0x7fffffffLL)
+            return KDA_ERR_UNSUPPORTED;
+    }
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     // the launches below are checked with hipGetLastError: drop an error another call of

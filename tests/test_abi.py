@@ -212,6 +212,14 @@ def test_decode_rejects_bad_arguments():
     assert dec(kda.config(4, head_dim=256)) == kda.ERR_UNSUPPORTED
 
 
+def test_scan_grid_limit():
+    """A named segmented prefill whose grids would not fit one 32-bit dimension (8 x N x H
+    workgroups for the scan) is refused after the workspace check and before any HIP call."""
+    n = 3_000_000  # 3M one-token sequences x 96 heads: 288M items, 2.3G scan workgroups
+    a = _args(num_seqs=n, total_tokens=n, workspace_bytes=1 << 62)
+    assert _prefill(kda.config(96, algo="chunked_scan"), a) == kda.ERR_UNSUPPORTED
+
+
 def test_no_alloc_validation():
     """kda_prefill_no_alloc validates like kda_prefill and ignores the caller's workspace;
     a configuration whose workspace exceeds the static scratch (the segmented prefill, when

@@ -13,10 +13,10 @@ HIP events on the launch stream), and the fp64 CPU oracle timed on one
 sequence of the same workload on the host's cores.  Also in the line: first,
 the measured ceilings of this GPU (a streaming HBM copy, an HBM read stream
 and a loop of bf16 matrix-core instructions), against which every fraction
-is also given beside the vendor's spec peaks; after the step loop, the
-long-context prefill (1 x 131072 tokens x 96 heads,
-random S0) and the packed variable-length prefill (64 lognormal lengths,
-578k tokens, per-sequence S0), each with its roofline fractions.
+is also given beside the vendor's spec peaks; then, before the step loop,
+the long-context prefill (1 x 131072 tokens x 96 heads, random S0) and the
+packed variable-length prefill (64 lognormal lengths, 578k tokens,
+per-sequence S0), each with its roofline fractions.
 
     python bench.py [--steps K] [--warmup W] [--algo auto|chunked|recurrent] [--no-long]
 """
@@ -203,11 +203,12 @@ def oracle_single_thread(W, oracle, decode_sample: int = 16) -> dict:
     return out
 
 
-def time_long_workload(kda, W, dev, stream, log, name, spec, algos, reps=3, warmup=1) -> dict:
+def time_long_workload(kda, W, dev, stream, log, name, spec, algos, reps=3, warmup=1, hold=None) -> dict:
     """Time one long prefill workload (all sequences start from a random S0): inputs are
     generated one sequence at a time (the seeded generator the parity tests use) straight
     into device buffers; each algorithm in `algos` is run `warmup` times, then timed over
-    `reps` launches with HIP events."""
+    `reps` launches with HIP events.  With a list `hold`, the device buffers are appended
+    to it rather than freed."""
     import torch
     out = {}
     lens = [int(x) for x in spec.lens]
@@ -260,8 +261,11 @@ def time_long_workload(kda, W, dev, stream, log, name, spec, algos, reps=3, warm
                     "frac_of_hbm_roofline": nb / (ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)}
         log(f"{key} ({ran}): {ms:.2f} ms, {T / (ms * 1e-3) / 1e6:.2f} M tokens/s")
         del ws
+    if hold is not None:
+        hold.append((bufs, la, beta, s0, o, s_out))
     del bufs, la, beta, s0, o, s_out
-    torch.cuda.empty_cache()
+    if hold is None:
+        torch.cuda.empty_cache()
     return out
 
 
@@ -590,6 +594,24 @@ def main() -> int:
     # (first: they characterise the machine the rest runs on)
     peaks = None if args.no_long else measure_peaks(dev, stream, log)
 
+    # ---------------------------------------------------------------- long launches
+    # The long-context and packed variable-length prefills, before the step loop, which
+    # then follows them without a pause: the GPU lowers its clock within a fraction of a
+    # second of idling and raises it again over tens of milliseconds of this kernel (right
+    # after a 0.3 s pause the 4 x 4096 prefill measured 1.8 ms on its second launch, 1.45 ms
+    # by its tenth and 1.29 ms from about its thirtieth).  Their buffers (about 100 GB) are
+    # therefore freed after the step loop: the frees take long enough to idle the GPU.
+    long_runs = None
+    held = []
+    if not args.no_long:
+        long_runs = {}
+        long_runs.update(time_long_workload(kda, W, dev, stream, log, "prefill_131072", W.workload("prefill_131072"),
+                                            [args.algo], reps=5, warmup=2))
+        long_runs.update(time_long_workload(kda, W, dev, stream, log, "varlen_64", W.workload("varlen_64"),
+                                            [args.algo], reps=5, warmup=2, hold=held))
+        for e in long_runs.values():
+            e["frac_of_measured_hbm"] = e["GBps"] / peaks["hbm_GBps"]
+
     # ---------------------------------------------------------------- timing
     for _ in range(args.warmup):
         run_prefill()
@@ -603,6 +625,8 @@ def main() -> int:
     wall = time.perf_counter() - t_wall0
     log(f"prefill {pre_mean:.3f} ms (median {pre_med:.3f}); decode {dec_mean:.4f} ms "
         f"(median {dec_med:.4f}); wall {wall:.2f}s")
+    held.clear()
+    torch.cuda.empty_cache()
 
     copy_cal = None
     if args.copy_calibration > 0:
@@ -647,16 +671,6 @@ def main() -> int:
         log(f"oracle, one thread: {json.dumps(cpu1)}")
 
     traffic = load_traffic(args.traffic)
-    # the long-context and packed variable-length launches, and this GPU's measured ceilings
-    long_runs = None
-    if not args.no_long:
-        long_runs = {}
-        long_runs.update(time_long_workload(kda, W, dev, stream, log, "prefill_131072", W.workload("prefill_131072"),
-                                            [args.algo], reps=5, warmup=2))
-        long_runs.update(time_long_workload(kda, W, dev, stream, log, "varlen_64", W.workload("varlen_64"),
-                                            [args.algo], reps=5, warmup=2))
-        for e in long_runs.values():
-            e["frac_of_measured_hbm"] = e["GBps"] / peaks["hbm_GBps"]
     extra = None
     if args.extra_workloads:
         extra = run_extra_workloads(kda, W, dev, stream, log, args.algo)

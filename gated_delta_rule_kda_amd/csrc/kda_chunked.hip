@@ -428,7 +428,7 @@ __global__ __launch_bounds__(THREADS, 4) void chunked_tp_kernel(LayerParams p) {
     };
     // At the start of chunk ch's Gram / T phase: the outputs of chunk ch - 1 (or the same
     // memory operations, dropped).  At the end of its state update: the g rows of chunk ch
-    // and the low-rank gate's z_down rows of chunk ch + 1, so that neither is held in
+    // and the low-rank gate's W_up operand for chunk ch + 1, so that neither is held in
     // registers through the triangular solve and the state products.
     auto epilogue_stage = [&](int ch) {
         if (epi_wave && do_epi && ch > 0)

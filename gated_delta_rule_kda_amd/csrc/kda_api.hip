@@ -138,15 +138,17 @@ ScanPlan scan_plan(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens
 // whose scratch cannot hold the segment matrices).  Measured with the full layer on bf16
 // inputs: at most 3/8 as many (sequence, head) items as CUs, over sequences averaging 1024
 // tokens or more, gain 1.1x (96 items of 4096 tokens: 0.92 -> 0.83 ms) to 4.5x (12 items
-// of 8192: 1.79 -> 0.40 ms), while 128 items of 4096 tokens lose 5-10%; with fewer items
-// than CUs, sequences averaging 16384 tokens or more gain (1 x 131072 x 96: 27.8 -> 20.4 ms).
+// of 8192: 1.79 -> 0.40 ms); at half as many items as CUs only long sequences gain (128
+// items of 32768 tokens: 7.08 -> 6.68 ms; of 4096: 0.93 -> 0.97 ms, a loss); with more
+// items the split loses at every length measured (160 items of 65536 tokens: 14.1 -> 16.2
+// ms; 192 of 32768: 7.1 -> 10.5 ms), since those items already occupy most CUs.
 int32_t resolve_algo(const kda_config *cfg, int32_t num_seqs, int64_t total_tokens, bool scan_ok = true) {
     int algo = cfg->algo;
     if (algo == KDA_ALGO_AUTO) algo = cfg->io_dtype == KDA_DTYPE_BF16 ? KDA_ALGO_CHUNKED : KDA_ALGO_RECURRENT;
     if (algo == KDA_ALGO_CHUNKED) {
         const int64_t items = static_cast<int64_t>(num_seqs) * cfg->num_heads;
         const bool few = items <= 3 * device_cu_count() / 8 && total_tokens >= 1024LL * num_seqs;
-        const bool long_seqs = items < device_cu_count() && total_tokens >= 16384LL * num_seqs;
+        const bool long_seqs = items <= device_cu_count() / 2 && total_tokens >= 16384LL * num_seqs;
         algo = scan_ok && scan_supported(cfg) && (few || long_seqs) ? KDA_ALGO_CHUNKED_SCAN
                                                                     : KDA_ALGO_CHUNKED_THROUGHPUT;
     }

@@ -109,7 +109,8 @@ typedef int32_t kda_status;
  * CHUNKED take it for bf16 inputs when one pass would leave most compute units idle:
  * at most 3/8 as many (sequence, head) items as compute units over sequences averaging
  * 1024 tokens or more (12 items of 8192 tokens: 4.5x faster; 96 items of 4096: 1.1x),
- * or fewer items than compute units over sequences averaging 16384 tokens or more.
+ * or at most half as many items as compute units over sequences averaging 16384 tokens
+ * or more (with more items the split measured slower at every length).
  * bf16 io and the LOG_ALPHA, LOWRANK and HEAD gates only; its M and B matrices live in
  * the workspace. */
 #define KDA_ALGO_CHUNKED_SCAN 5

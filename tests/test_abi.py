@@ -258,7 +258,7 @@ def test_resolved_algo():
 def test_scan_selection_and_workspace():
     """AUTO splits the sequences when one pass would leave most compute units idle (256
     when sized without a device): at most 96 (sequence, head) items over sequences
-    averaging 1024 tokens or more, or fewer than 256 items over sequences averaging 16384;
+    averaging 1024 tokens or more, or at most 128 items over sequences averaging 16384;
     the workspace then holds two 64 KiB matrices per (segment slot, head)."""
     c = kda.config(96)
     assert kda.resolved_algo(c, 1, 131072) == "chunked_scan"
@@ -268,6 +268,8 @@ def test_scan_selection_and_workspace():
     assert kda.resolved_algo(kda.config(12), 4, 4 * 4096) == "chunked_scan"   # 48 items
     assert kda.resolved_algo(kda.config(128), 1, 8192) == "chunked_throughput"  # 128 items
     assert kda.resolved_algo(kda.config(128), 1, 16384) == "chunked_scan"       # long
+    assert kda.resolved_algo(kda.config(192), 1, 32768) == "chunked_throughput"  # 192 items
+    assert kda.resolved_algo(kda.config(96), 2, 2 * 16384) == "chunked_throughput"
     assert kda.resolved_algo(kda.config(96, gate="head"), 1, 8192) == "chunked_scan"
     assert kda.resolved_algo(kda.config(96, io_dtype="f32"), 1, 131072) == "recurrent"
     assert kda.resolved_algo(kda.config(96, gate="lowrank_softplus"), 1, 131072) == "chunked_throughput"

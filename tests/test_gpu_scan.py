@@ -180,3 +180,27 @@ def test_auto_splits_few_items():
     for a, b in zip(na, tp):
         assert torch.equal(a, b)
     assert err(to_np(na[0]), r["o"]) <= TOL
+
+
+def test_tp_share_auto_deterministic():
+    """The 4 x 4096 prefill at 12 heads (its share of one GPU under 8-way tensor
+    parallelism), AUTO algorithm (the segmented prefill): two launches bitwise equal (no
+    atomics, fixed orders), and heads 0 and 11 of sequences 0 and 3 against the oracle."""
+    import torch
+    import gated_delta_rule_kda_amd as kda
+    from kda_testlib import err_bf16, gpu_rows, subset
+    spec = W.PrefillSpec(lens=[4096] * 4, heads=12, seed=127)
+    assert kda.resolved_algo(kda.config(12), 4, 4 * 4096) == "chunked_scan"
+    inp = W.gen_prefill(spec)
+    say("4 x 4096 x 12: gpu (twice)")
+    o1, s1, c1 = gpu_prefill(inp, io="bf16", out="bf16", algo="auto", keep_device=True)
+    o2, s2, c2 = gpu_prefill(inp, io="bf16", out="bf16", algo="auto", keep_device=True)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(c1, c2), "not deterministic"
+    g = dict(o=to_np(o1), state=to_np(s1), conv=to_np(c1))
+    for seqs, heads in (([0], [0, 11]), ([3], [0, 11])):
+        r = oracle_prefill(subset(inp, seqs, heads))
+        gs = gpu_rows(g, inp, seqs, heads)
+        eo, es = err_bf16(gs["o"], r["o"]), err(gs["state"], r["state"])
+        say(f"  seqs {seqs} heads {heads}: o err {eo:.2e}  S err {es:.2e}")
+        assert eo <= TOL and es <= TOL
+        assert np.array_equal(gs["conv"], r["conv"])

@@ -253,7 +253,7 @@ def time_long_workload(kda, W, dev, stream, log, name, spec, algos, reps=3, warm
         nb = prefill_algorithmic_bytes(T, H, N) + N * H * D * D * 4  # + the initial states read
         key = name if a == algos[0] else f"{name}_{a}"
         ran = kda.resolved_algo(cfg, N, T)
-        out[key] = {"workload": f"{N} x {T // N if N == 1 else 'lognormal'} tokens, H={H}, d=128, full layer, "
+        out[key] = {"workload": f"{N} x {lens[0] if len(set(lens)) == 1 else 'lognormal'} tokens, H={H}, d=128, full layer, "
                                 f"bf16 io, random fp32 S0", "tokens": T, "sequences": N, "heads": H,
                     "max_len": max(lens), "algo": ran, "ms": ms, "ms_median": med, "reps": reps,
                     "tokens_per_s": T / (ms * 1e-3), "algorithmic_bytes": nb,
@@ -272,7 +272,8 @@ def time_long_workload(kda, W, dev, stream, log, name, spec, algos, reps=3, warm
 def run_extra_workloads(kda, W, dev, stream, log, algo="auto") -> dict:
     """The long context in one sequential pass (the chunked kernel, next to AUTO's
     segmented prefill in the main line) and at 12 heads (one GPU's share of 96 heads split
-    eight ways), by AUTO and in one pass."""
+    eight ways), by AUTO and in one pass; and the 4 x 4096 prefill at 12 heads, by AUTO
+    (the segmented prefill) and in one pass."""
     import dataclasses
     out = {}
     long12 = dataclasses.replace(W.workload("prefill_131072"), heads=12, name="prefill_131072_h12")
@@ -280,6 +281,9 @@ def run_extra_workloads(kda, W, dev, stream, log, algo="auto") -> dict:
                                   ["chunked_throughput"]))
     out.update(time_long_workload(kda, W, dev, stream, log, "prefill_131072_h12", long12,
                                   [algo, "chunked_throughput"]))
+    share12 = dataclasses.replace(W.workload("prefill_4x4096"), heads=12, state_std=0.02, name="prefill_4x4096_h12")
+    out.update(time_long_workload(kda, W, dev, stream, log, "prefill_4x4096_h12", share12,
+                                  [algo, "chunked_throughput"], reps=20, warmup=20))
     return out
 
 

@@ -312,3 +312,16 @@ def test_varlen_full_size_sampled():
         say(f"  sequence {n} ({lens[n]} tokens) head {h}: o err {eo:.2e}  S err {es:.2e}")
         assert eo <= BF16_TOL and es <= BF16_TOL
     assert torch.isfinite(o).all()
+
+
+def test_many_sequences_natural_order():
+    """More sequences (8200, of 0 to 40 tokens) than the longest-first order table holds:
+    the kernels take the sequences in their natural order, with no workspace."""
+    import gated_delta_rule_kda_amd as kda
+    lens = [int(x) for x in np.random.default_rng(131).integers(0, 41, 8200)]
+    assert kda.workspace_size(kda.config(1), len(lens), sum(lens)) == 0
+    inp = W.gen_prefill(W.PrefillSpec(lens=lens, heads=1, state_std=0.05, conv_in=True, seed=132))
+    say(f"8200 sequences, {sum(lens)} tokens")
+    g = gpu_prefill(inp, io="bf16", out="f32", algo="auto")
+    r = oracle_prefill(inp)
+    _check(g, r, "f32")

@@ -188,6 +188,16 @@ def _expect(t, name: str, dtype, shape=None) -> None:
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
+def _expect_device(dev, **tensors) -> None:
+    """Every tensor given lives on `dev`, the GPU of q: the kernels take raw device pointers,
+    so a host tensor or one on another GPU would be read as an address on this one."""
+    if dev.type != "cuda":
+        raise ValueError(f"q is on {dev}: the inputs must be GPU tensors")
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev} (the device of q)")
+
+
 def _expect_gate(cfg, z, w, bias, a, T, H, io_t) -> None:
     import torch
     r = cfg.gate_rank
@@ -271,6 +281,11 @@ def prefill(q, k, v, log_alpha, beta, cu_seqlens, *, g=None, conv_w=None, conv_i
     _expect(o, "o", out_t, (T, H, D))
     _expect(state_out, "state_out", torch.float32, (rows_out, H, D, D))
     _expect(conv_out, "conv_out", io_t, (rows_co, 3, 3, H * D))
+    _expect_device(dev, q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, cu_seqlens=cu_seqlens, g=g,
+                   conv_w=conv_w, conv_in=conv_in, conv_out=conv_out, rms_w=rms_w, state_in=state_in,
+                   state_out=state_out, o=o, workspace=workspace, state_in_slots=state_in_slots,
+                   state_out_slots=state_out_slots, gate_z=gate_z, gate_w=gate_w, gate_bias=gate_bias,
+                   gate_a=gate_a)
     a = PrefillArgs()
     a.num_seqs, a.cu_seqlens, a.total_tokens = N, _ptr(cu_seqlens), T
     a.q, a.k, a.v, a.log_alpha, a.beta, a.g = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
@@ -329,6 +344,9 @@ def decode_step(q, k, v, log_alpha, beta, state, *, g=None, conv_w=None, conv_st
         with _on_stream(stream):
             o = torch.empty((B, H, D), dtype=out_t, device=q.device)
     _expect(o, "o", out_t, (B, H, D))
+    _expect_device(q.device, q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, g=g, conv_w=conv_w,
+                   conv_state=conv_state, rms_w=rms_w, state=state, slots=slots, slots_out=slots_out, o=o,
+                   gate_z=gate_z, gate_w=gate_w, gate_bias=gate_bias, gate_a=gate_a)
     a = DecodeArgs()
     a.batch = B
     a.q, a.k, a.v, a.log_alpha, a.beta, a.g = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),

@@ -325,3 +325,20 @@ def test_unbounded_gate_arguments():
     bad = kda.config(4)
     bad.gate = 5
     assert _prefill(bad, _args()) == kda.ERR_INVALID_ARGUMENT
+
+
+def test_binding_refuses_tensors_off_the_gpu():
+    """The binding passes raw pointers: a host tensor is refused before any library call."""
+    import torch
+    T, H = 16, 2
+    bf = torch.bfloat16
+    q, k, v, g = (torch.zeros((T, H, 128), dtype=bf) for _ in range(4))
+    la = torch.zeros((T, H, 128), dtype=torch.float32)
+    beta = torch.zeros((T, H), dtype=torch.float32)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    cw = torch.zeros((3, H * 128, 4), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        kda.prefill(q, k, v, la, beta, cu, g=g, conv_w=cw)
+    st = torch.zeros((T, H, 128, 128), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        kda.decode_step(q, k, v, la, beta, st, g=g, conv_w=cw, conv_state=torch.zeros((T, 3, 3, H * 128), dtype=bf))
